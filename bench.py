@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode-attention layer step over a long KV cache on one MI355X.
+
+A step is one pass of the whole path over one batch: kvd_decode_partial
+(split-KV partial attention for every request, KV head and shard) followed by
+kvd_lse_merge (exact merge of the shards), both through the C ABI on one HIP
+stream, with the synthetic cache already resident in HBM.  The default
+workload is the Helix Figure-1 dense shape on one GPU: B=8 requests, 128
+query heads on 8 KV heads, Hsz=128, S=2^20 tokens each, fp8 E4M3 cache with
+one fp32 scale per (request, KV head), bf16 queries, KVP=32 shards.
+
+Prints one JSON line.  `value` is KV-read GB/s: the algorithmic cache bytes of
+one step (every cached element read once) divided by the measured time per
+step.  The roofline object is for the dominant kernel (the partial pass),
+timed with HIP events on the stream it runs on; its `traffic` field comes from
+rocprofv3 counters recorded separately (null when no counter run matches the
+current kernel).  The cpu_baseline object times the float64 CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S=1M GQA"
+
+# HBM bytes per launch of the partial kernel measured with rocprofv3 counters,
+# keyed by (workload, kvp, kernel revision); see profiles/.
+TRAFFIC = {}
+KERNEL_REVISION = "valu-1"
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, target_s=15.0):
+    """Time the float64 oracle on whole (request, KV head) slabs until ~target_s
+    of CPU work, and scale to KV GB/s."""
+    import numpy as np
+
+    import kvgen
+    import oracle
+    from long_context_decode_split_amd import roofline
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    q = kvgen.gen_q(w)
+    seq = kvgen.gen_seq_lens(w)
+    p = oracle.Problem.from_workload(w)
+    G = w.G
+    done_bytes, elapsed, slabs = 0, 0.0, 0
+    pairs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    for (b, kvh) in pairs:
+        kd, ks = kvgen.gen_kv_slab(w, "k", b, kvh)
+        vd, vs = (None, None) if w.v_aliases_k else kvgen.gen_kv_slab(w, "v", b, kvh)
+        L = int(seq[b])
+        t0 = time.perf_counter()
+        if w.kv_dtype == "mxfp4":
+            k = oracle.dequant("mxfp4", kd[:L], ks[:L], w.Dqk)
+            v = k[:, :w.Dv] if w.v_aliases_k else oracle.dequant("mxfp4", vd[:L], vs[:L], w.Dv)
+        else:
+            k = oracle.dequant(w.kv_dtype, kd[:L], ks, w.Dqk)
+            v = k[:, :w.Dv] if w.v_aliases_k else oracle.dequant(w.kv_dtype, vd[:L], vs, w.Dv)
+        qf = oracle.q_to_f64(q[b, kvh * G:(kvh + 1) * G], w.q_dtype)
+        oracle.attend(qf, k, v, p.sm_scale)
+        elapsed += time.perf_counter() - t0
+        done_bytes += roofline.kv_bytes(1, [L], w.Dqk, w.Dv, w.kv_dtype, w.v_aliases_k)
+        slabs += 1
+        del k, v
+        if elapsed >= target_s:
+            break
+    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": int(max(cores, blas_threads)),
+            "blas_threads": int(blas_threads), "host_cpus": int(cores), "kind": "oracle",
+            "sample": "%d of %d (request, KV head) slabs of %s, full length each, float64 dequant + "
+                      "attention, %.1f s" % (slabs, len(pairs), w.name, elapsed),
+            "seconds": elapsed, "bytes": int(done_bytes)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="helix_fp8")
+    ap.add_argument("--kvp", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU's share of the split-KV path; runs on more than one GPU "
+              "are not part of this build (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kvgen
+    from kvgen.device import generate_on_device
+    from long_context_decode_split_amd import kvd, roofline
+
+    w = kvgen.WORKLOADS[args.workload]
+    kvp = args.kvp or (32 if 32 in w.kvp else w.kvp[0])
+    torch.cuda.set_device(0)
+    log("generating %s (kvp=%d) into device memory" % (w.name, kvp))
+    t0 = time.time()
+    dev = generate_on_device(w, progress=log)
+    log("inputs ready in %.1f s" % (time.time() - t0))
+
+    p = kvd.problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, w.S_max, kvp, w.q_dtype, w.kv_dtype, 0.0, w.v_aliases_k)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o_part = torch.empty((kvp, w.B, w.Hq, w.Dv), **f32)
+    lse_part = torch.empty((kvp, w.B, w.Hq), **f32)
+    o = torch.empty((w.B, w.Hq, w.Dv), **f32)
+    lse = torch.empty((w.B, w.Hq), **f32)
+    rows = w.B * w.Hq
+    stream = torch.cuda.Stream()
+    seq = dev.seq_lens.cpu().numpy()
+    kv_bytes = roofline.kv_bytes(w.Hkv, seq, w.Dqk, w.Dv, w.kv_dtype, w.v_aliases_k)
+    flops = roofline.attention_flops(w.Hq, seq, w.Dqk, w.Dv)
+
+    def step(ev0=None, ev1=None, ev2=None):
+        if ev0 is not None:
+            ev0.record(stream)
+        kvd.kvd_decode_partial(p, dev.q, dev.k, dev.v, dev.seq_lens, o_part, lse_part, stream)
+        if ev1 is not None:
+            ev1.record(stream)
+        kvd.kvd_lse_merge(kvp, rows, w.Dv, o_part, lse_part, o, lse, stream)
+        if ev2 is not None:
+            ev2.record(stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            step(*evs[i])
+        end.record(stream)
+        torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    partial_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    partial_avg = sum(partial_ms) / len(partial_ms)
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
+
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (partial_avg * 1e-3) / 1e9
+    peak = roofline.HBM_BYTES_PER_S / 1e9
+    traffic = TRAFFIC.get((w.name, kvp, KERNEL_REVISION))
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_peak_frac": round(value / peak, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1), encoded to the cache format)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Hsz": w.Dqk, "Dv": w.Dv,
+                   "S": w.S_max, "kvp": kvp, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
+                   "kv_bytes": kv_bytes, "flops": flops},
+        "partial_us": round(partial_avg * 1e3, 2),
+        "merge_us": round(sum(merge_ms) / len(merge_ms) * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": peak, "unit": "GB/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "kvd partial pass", "bytes_per_launch": kv_bytes,
+                     "tflops": round(flops / (partial_avg * 1e-3) / 1e12, 2)},
+    }
+    del dev
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

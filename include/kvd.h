@@ -1,0 +1,149 @@
+/*
+ * kvd.h — exact split-KV decode attention on MI355X (gfx950): the C ABI of libkvd.so.
+ *
+ * The operation.  One new query token per request attends to every cached
+ * token of that request: for query head h of request b, with KV head
+ * kvh = floor(h / G), G = Hq / Hkv, and L = seq_lens[b],
+ *     x_s = sm_scale * <q[b,h,:], k[b,kvh,s,:]>          s = 0 .. L-1
+ *     o[b,h,:] = sum_s softmax(x)_s * v[b,kvh,s,:],  lse[b,h] = ln sum_s exp(x_s)
+ * i.e. softmax(q K^T / sqrt(d)) V for a single query row (sm_scale defaults to
+ * 1/sqrt(Dqk)).  Grouped-query attention maps consecutive query heads onto one
+ * KV head; multi-head latent attention is the case Hkv = 1 with V the first Dv
+ * columns of the cached latent K.
+ *
+ * The split.  Following KV parallelism in "Helix Parallelism: Why Tensor
+ * Parallelism Hits a Wall at Million-Token Context" (section "Sharding the
+ * sequence instead"), the sequence of each request is cut into kvp shards;
+ * each shard yields its own normalized partial output and the log-sum-exp of
+ * its logits, and a log-sum-exp merge of the shards gives the exact
+ * full-context result (same article, the merge sketch; and the exact merge
+ * equation in the "Context Parallelism for Scalable Million-Token Inference"
+ * note, section "Pass-KV keeps queries local and circulates keys and values").
+ * Shard j of a request with L tokens covers tokens [j*C, min(L, (j+1)*C)),
+ * C = ceil(ceil(L / kvp) / 16) * 16; a shard starting at or past L is empty
+ * and yields o = 0, lse = -inf (weight zero in the merge).  Partials are laid
+ * out shard-major, so shard j's block is exactly what KV-parallel rank j would
+ * send in the all-to-all.
+ *
+ * Conventions for every entry point:
+ *  - Ownership: every pointer argument (except `p`, which is host memory) is a
+ *    caller-owned DEVICE pointer.  The library never allocates, frees or
+ *    synchronizes; it keeps no state between calls and is reentrant.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *    stream) and the call returns without waiting for it.
+ *  - Layouts: contiguous row-major.  q [B,Hq,Dqk]; k.data [B,Hkv,S_max,Dqk];
+ *    v.data [B,Hkv,S_max,Dv]; seq_lens int32 [B]; outputs are fp32:
+ *    o [B,Hq,Dv], lse [B,Hq] (natural log), o_part [kvp,B,Hq,Dv],
+ *    lse_part [kvp,B,Hq].
+ *  - KV formats (kv_dtype):
+ *      KVD_F32, KVD_BF16: plain elements; scale must be NULL.
+ *      KVD_FP8_E4M3: OCP E4M3 ("fn") codes, one byte per element; scale is a
+ *        float [B,Hkv] per tensor: element value = code value * scale[b,kvh].
+ *      KVD_MXFP4: OCP MXFP4; data rows hold D/2 bytes, element 2i in bits
+ *        [3:0] and 2i+1 in bits [7:4] of byte i; scale is uint8 E8M0
+ *        [B,Hkv,S_max,D/32], value 2^(E-127) for the 32 contiguous elements
+ *        of its block.  Requires D % 32 == 0.
+ *  - Alignment: q, k.data, v.data, o, o_part and workspace must be 16-byte
+ *    aligned; seq_lens, lse, lse_part and scale pointers 4-byte aligned.
+ *  - Errors: every argument is validated on the host before anything is
+ *    enqueued; an invalid call returns KVD_ERR_INVALID (malformed) or
+ *    KVD_ERR_UNSUPPORTED (well formed, but no kernel of this build handles it)
+ *    and enqueues nothing.  A launch failure reported by the HIP runtime
+ *    returns KVD_ERR_HIP.  kvd_last_error() gives the calling thread's message
+ *    for its last failed call.
+ *  - Device-side preconditions: 0 <= seq_lens[b] <= S_max.  Kernels clamp
+ *    each length into [0, S_max], so no read ever leaves the cache.  A
+ *    request with L = 0 yields o = 0 and lse = -inf.
+ */
+#ifndef KVD_H_
+#define KVD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVD_ABI_VERSION 1
+
+typedef enum {
+  KVD_OK = 0,
+  KVD_ERR_INVALID = 1,
+  KVD_ERR_UNSUPPORTED = 2,
+  KVD_ERR_HIP = 3
+} kvd_status;
+
+typedef enum {
+  KVD_F32 = 0,
+  KVD_BF16 = 1,
+  KVD_FP8_E4M3 = 2,
+  KVD_MXFP4 = 3
+} kvd_dtype;
+
+/* A hipStream_t (layout-compatible; NULL is the null stream). */
+typedef struct ihipStream_t* kvd_stream_t;
+
+/* Shape of one decode step: B requests, Hq query heads on Hkv KV heads of
+ * widths Dqk (q, k) and Dv (v, o), cache stride S_max tokens, kvp shards. */
+typedef struct {
+  int32_t B;            /* requests, >= 1 */
+  int32_t Hq;           /* query heads, >= 1, Hq % Hkv == 0 */
+  int32_t Hkv;          /* KV heads, >= 1 */
+  int32_t Dqk;          /* q/k head width */
+  int32_t Dv;           /* v/o head width (== Dqk except latent attention) */
+  int64_t S_max;        /* token stride of the cache, >= 1, >= every seq_len */
+  int32_t kvp;          /* shards per request, 1 .. 4096 */
+  int32_t q_dtype;      /* kvd_dtype: KVD_F32 or KVD_BF16 */
+  int32_t kv_dtype;     /* kvd_dtype of K and V */
+  float sm_scale;       /* logit scale, >= 0 and finite; 0 means 1/sqrt(Dqk) */
+  int32_t v_aliases_k;  /* nonzero: V is k[..., :Dv] (Dv <= Dqk); v.data and
+                           v.scale must be NULL */
+} kvd_problem;
+
+/* One cache tensor: element data and, for fp8 / MXFP4, its scales. */
+typedef struct {
+  const void* data;
+  const void* scale;
+} kvd_kv;
+
+/* Shard partials: for every request b, shard j < kvp and query head h,
+ * o_part[j,b,h,:] = softmax-weighted mean of V over shard j's tokens (fp32)
+ * and lse_part[j,b,h] = ln sum over shard j of exp(x_s) (fp32), i.e. the
+ * (o_local, lse_local) pair each KV-parallel rank produces. */
+int kvd_decode_partial(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
+                       const int32_t* seq_lens, float* o_part, float* lse_part,
+                       kvd_stream_t stream);
+
+/* Exact log-sum-exp merge of kvp partials for `rows` independent rows:
+ * M = max_j lse_part[j,r]; w_j = exp(lse_part[j,r] - M) (0 for an empty
+ * shard); o[r,:] = sum_j w_j o_part[j,r,:] / sum_j w_j; lse[r] = M + ln sum_j
+ * w_j; rows whose shards are all empty give o = 0, lse = -inf.  o_part is
+ * [kvp,rows,Dv], lse_part [kvp,rows]; Dv % 4 == 0; rows may be 0. */
+int kvd_lse_merge(int32_t kvp, int64_t rows, int32_t Dv, const float* o_part,
+                  const float* lse_part, float* o, float* lse, kvd_stream_t stream);
+
+/* Bytes of device workspace kvd_decode needs for problem p (the shard
+ * partials, 256-byte aligned pieces); 0 if p is invalid. */
+size_t kvd_decode_workspace_bytes(const kvd_problem* p);
+
+/* kvd_decode_partial into `workspace` followed by kvd_lse_merge into o, lse,
+ * both on `stream`: the exact full-context result. */
+int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
+               const int32_t* seq_lens, void* workspace, float* o, float* lse,
+               kvd_stream_t stream);
+
+/* Static description of a status code. */
+const char* kvd_status_string(int status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* kvd_last_error(void);
+
+/* KVD_ABI_VERSION of the library. */
+int kvd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVD_H_ */

@@ -1,0 +1,152 @@
+// Device-side helpers shared by the libkvd kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum KvFormat : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kMXFP4 = 3 };
+
+// Bytes of one cached element (MXFP4 counts half a byte: use row bytes).
+template <int KV>
+struct KvTraits;
+template <>
+struct KvTraits<kF32> { static constexpr int kBitsPerElem = 32; };
+template <>
+struct KvTraits<kBF16> { static constexpr int kBitsPerElem = 16; };
+template <>
+struct KvTraits<kFP8> { static constexpr int kBitsPerElem = 8; };
+template <>
+struct KvTraits<kMXFP4> { static constexpr int kBitsPerElem = 4; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// E8M0 block exponent -> fp32 scale 2^(E-127).  E = 0 is the subnormal
+// 2^-127 and E = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  float s = __uint_as_float(e << 23);
+  s = (e == 0u) ? __uint_as_float(0x00400000u) : s;
+  s = (e == 255u) ? __uint_as_float(0x7FC00000u) : s;
+  return s;
+}
+
+// Load N bytes (N in {4, 8, 16, 32, 64}) from a 4-byte-aligned (N >= 16:
+// 16-byte aligned) global address into N/4 dwords.
+template <int N>
+__device__ __forceinline__ void load_dwords(const uint8_t* __restrict__ p, uint32_t* w) {
+  static_assert(N % 4 == 0 && N >= 4, "whole dwords only");
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int i = 0; i < N / 16; ++i) {
+      uint4 v = *reinterpret_cast<const uint4*>(p + 16 * i);
+      w[4 * i + 0] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (N == 8) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// Decode EPL consecutive elements held in dwords w (format KV) to fp32.
+// fp8 scales are applied by the caller; the MXFP4 block scale is applied here.
+template <int KV, int EPL>
+__device__ __forceinline__ void decode_elems(const uint32_t* w, float mx_scale, float* out) {
+  if constexpr (KV == kF32) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = __uint_as_float(w[e]);
+  } else if constexpr (KV == kBF16) {
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+      out[2 * i] = bf16_lo(w[i]);
+      out[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else if constexpr (KV == kFP8) {
+#pragma unroll
+    for (int i = 0; i < EPL / 4; ++i) {
+      auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+      auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+      out[4 * i + 0] = lo[0];
+      out[4 * i + 1] = lo[1];
+      out[4 * i + 2] = hi[0];
+      out[4 * i + 3] = hi[1];
+    }
+  } else {
+    static_assert(KV == kMXFP4, "format");
+#pragma unroll
+    for (int i = 0; i < EPL / 8; ++i) {
+      auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], mx_scale, 0);
+      auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], mx_scale, 1);
+      auto b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], mx_scale, 2);
+      auto b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], mx_scale, 3);
+      out[8 * i + 0] = b0[0];
+      out[8 * i + 1] = b0[1];
+      out[8 * i + 2] = b1[0];
+      out[8 * i + 3] = b1[1];
+      out[8 * i + 4] = b2[0];
+      out[8 * i + 5] = b2[1];
+      out[8 * i + 6] = b3[0];
+      out[8 * i + 7] = b3[1];
+    }
+  }
+}
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the result.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Weight 2^(m - M) of a running state with max m inside a merged max M
+// (zero when the state has seen no token, m = -inf).
+__device__ __forceinline__ float rescale_weight(float m, float M) {
+  return (m == -INFINITY) ? 0.0f : fast_exp2(m - M);
+}
+
+// Token range [s0, s1) of shard j of an L-token request split kvp ways:
+// C = ceil(ceil(L / kvp) / 16) * 16, shard j = [j*C, min(L, (j+1)*C)).
+__device__ __forceinline__ void shard_range(int64_t L, int kvp, int j, int64_t* s0, int64_t* s1) {
+  int64_t per = (L + kvp - 1) / kvp;
+  int64_t C = (per + 15) / 16 * 16;
+  int64_t a = (int64_t)j * C;
+  int64_t b = a + C;
+  *s0 = a < L ? a : L;
+  *s1 = b < L ? b : L;
+}
+
+}  // namespace kvd

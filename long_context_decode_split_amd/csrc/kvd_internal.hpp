@@ -1,0 +1,40 @@
+// Host-side interface between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvd {
+
+// Arguments of one split-KV partial pass, already validated by api.cpp.
+struct PartialArgs {
+  const void* q;
+  const void* k;
+  const void* k_scale;
+  const void* v;          // == k when V aliases K
+  const void* v_scale;    // == k_scale when V aliases K
+  const int32_t* seq_lens;
+  float* o_part;
+  float* lse_part;
+  int32_t B, Hq, Hkv, Dqk, Dv, kvp;
+  int64_t S_max;
+  int32_t q_bf16;         // q is bf16 (else fp32)
+  int32_t kv_format;      // KvFormat
+  int32_t v_aliases_k;
+  float scale_log2;       // sm_scale * log2(e)
+};
+
+// Each family reports whether it handles a problem, then launches it.
+bool valu_supports(const PartialArgs& a);
+hipError_t launch_partial_valu(const PartialArgs& a, hipStream_t stream);
+
+bool gqa_mfma_supports(const PartialArgs& a);
+hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream);
+
+bool mla_mfma_supports(const PartialArgs& a);
+hipError_t launch_partial_mla_mfma(const PartialArgs& a, hipStream_t stream);
+
+hipError_t launch_lse_merge(int32_t kvp, int64_t rows, int32_t Dv, const float* o_part,
+                            const float* lse_part, float* o, float* lse, hipStream_t stream);
+
+}  // namespace kvd

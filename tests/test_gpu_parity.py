@@ -1,0 +1,168 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Small cases compare every output and every shard partial element by element;
+they span several tiles, ragged tails, empty requests and empty shards.  The
+full-size workloads compare sampled (request, KV head) slabs, regenerated on
+the host and run through the oracle, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+
+import kvgen
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+
+def W(name, **kw):
+    base = dict(B=3, Hq=16, Hkv=2, Dqk=128, Dv=128, S_max=300, kvp=(4,), q_dtype="bf16",
+                kv_dtype="bf16", seed=7, seq_lens=(300, 17, 129))
+    base.update(kw)
+    return kvgen.Workload(name, **base)
+
+
+# ------------------------------------------------------------- small cases
+def test_mqa_f32_workload():
+    """The MQA fp32 workload (B=1, 8 heads on 1 KV head, Hsz=64, S=4096) at its KVP=4 and others."""
+    w = kvgen.WORKLOADS["mqa_f32"]
+    for kvp in (4, 1, 3, 16):
+        gc.check_full(w, kvp)
+
+
+SWEEP = []
+for kv in ("f32", "bf16", "fp8", "mxfp4"):
+    for D in (64, 128):
+        if kv == "mxfp4" and D == 64:
+            continue
+        for G in (1, 4, 8, 16):
+            SWEEP.append((kv, D, G))
+
+
+@pytest.mark.parametrize("kv,D,G", SWEEP, ids=lambda x: str(x))
+def test_sweep(kv, D, G):
+    Hkv = 2
+    for q_dtype in ("bf16", "f32"):
+        w = W("sweep_%s_d%d_g%d_%s" % (kv, D, G, q_dtype), Hq=G * Hkv, Hkv=Hkv, Dqk=D, Dv=D,
+              kv_dtype=kv, q_dtype=q_dtype, seq_lens=(300, 1, 17), seed=100 + G + D)
+        for kvp in (1, 3, 16):
+            gc.check_full(w, kvp)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
+def test_group16_long_ragged(kv):
+    """G=16 at a few thousand tokens with lengths off every tile boundary."""
+    w = W("g16_%s" % kv, B=2, Hq=32, Hkv=2, S_max=5000, seq_lens=(4999, 2049), kv_dtype=kv, seed=9)
+    for kvp in (1, 7, 32):
+        gc.check_full(w, kvp)
+
+
+def test_lengths_at_tile_edges():
+    for L in (1, 15, 16, 17, 31, 32, 33, 63, 64, 65):
+        w = W("edge_%d" % L, B=1, Hq=16, Hkv=1, S_max=80, seq_lens=(L,), kv_dtype="bf16", seed=L)
+        for kvp in (1, 2, 5):
+            gc.check_full(w, kvp)
+
+
+def test_empty_request_and_empty_shards():
+    """seq_len 0 gives o = 0, lse = -inf; lengths below kvp*16 leave empty shards."""
+    for kv in ("f32", "bf16", "fp8", "mxfp4"):
+        w = W("empty_%s" % kv, B=3, Hq=16, Hkv=1, S_max=64, seq_lens=(0, 5, 40), kv_dtype=kv)
+        gc.check_full(w, 16)
+        gc.check_full(w, 128)
+
+
+def test_poisoned_tail_is_never_read():
+    """Tokens past each request's length hold NaN codes; outputs stay finite and exact."""
+    for kv in ("f32", "bf16", "fp8", "mxfp4"):
+        w = W("poison_%s" % kv, B=3, Hq=16, Hkv=1, S_max=200, seq_lens=(1, 77, 150), kv_dtype=kv)
+        gc.check_full(w, 3, poison=True)
+
+
+def test_v_aliases_k_square():
+    w = W("alias", B=2, Hq=8, Hkv=1, Dqk=128, Dv=128, S_max=100, seq_lens=(100, 33),
+          kv_dtype="bf16", v_aliases_k=True)
+    gc.check_full(w, 3)
+
+
+def test_repeat_runs_bitwise_identical():
+    from kvgen.device import upload
+    w = W("det", kv_dtype="fp8", S_max=2000, seq_lens=(2000, 1999, 1000))
+    dev = upload(kvgen.make_inputs(w))
+    a = gc.run_library(dev, 8)
+    b = gc.run_library(dev, 8)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y, equal_nan=True)
+
+
+# -------------------------------------------------- full-size workloads
+_DEV_CACHE = {}
+
+
+def _device_inputs(name):
+    from kvgen.device import generate_on_device
+    import torch
+    if name not in _DEV_CACHE:
+        _DEV_CACHE.clear()
+        torch.cuda.empty_cache()
+        gc.log("generating %s on the host, slab by slab" % name)
+        _DEV_CACHE[name] = generate_on_device(kvgen.WORKLOADS[name], progress=gc.log)
+    return _DEV_CACHE[name]
+
+
+def _check_sampled(name, kvp, n_pairs=3):
+    dev = _device_inputs(name)
+    w = dev.workload
+    gc.log("%s kvp=%d: running the library" % (name, kvp))
+    o_part, lse_part, o, lse = gc.run_library(dev, kvp)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    # any-size property: merged lse >= every shard lse, and equals their log-sum-exp
+    lp = lse_part.astype(np.float64)
+    assert (lse[None] >= np.where(np.isfinite(lp), lp, -np.inf) - 1e-4).all()
+    q_np = dev.q.cpu().numpy()
+    if w.q_dtype == "bf16":
+        q_np = q_np.view(np.uint16)
+    seq = dev.seq_lens.cpu().numpy()
+    G = w.G
+    for (b, kvh) in gc.sampled_pairs(w, n_pairs):
+        gc.log("  oracle on request %d, KV head %d (L=%d)" % (b, kvh, seq[b]))
+        ro, rl, parts = gc.oracle_slab(w, b, kvh, seq[b], q_np, kvp)
+        hs = slice(kvh * G, (kvh + 1) * G)
+        gc.compare(o[b, hs], lse[b, hs], ro, rl, w.kv_dtype, "%s kvp=%d b=%d kvh=%d" % (name, kvp, b, kvh))
+        po = np.stack([p_[0] for p_ in parts])
+        pl = np.stack([p_[1] for p_ in parts])
+        gc.compare(o_part[:, b, hs], lse_part[:, b, hs], po, pl, w.kv_dtype,
+                   "%s kvp=%d b=%d kvh=%d partials" % (name, kvp, b, kvh))
+
+
+@pytest.mark.slow
+def test_full_gqa_bf16_varlen():
+    _check_sampled("gqa_bf16_varlen", 16)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("kvp", [8, 32, 128])
+def test_full_helix_fp8(kvp):
+    _check_sampled("helix_fp8", kvp, n_pairs=2)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("kvp", [8, 32, 128])
+def test_full_helix_mxfp4(kvp):
+    _check_sampled("helix_mxfp4", kvp, n_pairs=2)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["mxfp4_b1_s256k", "mxfp4_b32_s256k"])
+def test_full_mxfp4_batch_sweep(name):
+    _check_sampled(name, 32, n_pairs=2)
+
+
+@pytest.mark.slow
+def test_full_mla_bf16():
+    from long_context_decode_split_amd import kvd
+    w = kvgen.WORKLOADS["mla_bf16"]
+    p = gc.problem_of(w, 32)
+    import ctypes
+    if kvd.lib().kvd_decode_workspace_bytes(ctypes.byref(p)) == 0:
+        pytest.fail("invalid MLA problem")
+    _check_sampled("mla_bf16", 32, n_pairs=2)
