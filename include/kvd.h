@@ -51,6 +51,11 @@
  *    and enqueues nothing.  A launch failure reported by the HIP runtime
  *    returns KVD_ERR_HIP.  kvd_last_error() gives the calling thread's message
  *    for its last failed call.
+ *  - Kernel choice: the library picks the fastest kernel that handles the
+ *    problem (matrix-core kernels for 16-head GQA groups and for 576/512
+ *    latent heads, the vector-ALU kernel otherwise).  Setting the environment
+ *    variable KVD_PATH=valu before the first call restricts it to the
+ *    vector-ALU kernel, e.g. to cross-check the two.
  *  - Device-side preconditions: 0 <= seq_lens[b] <= S_max.  Kernels clamp
  *    each length into [0, S_max], so no read ever leaves the cache.  A
  *    request with L = 0 yields o = 0 and lse = -inf.

@@ -7,6 +7,8 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "kvd.h"
 #include "kvd_internal.hpp"
@@ -126,9 +128,22 @@ kvd::PartialArgs make_args(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv
 
 enum class Path { kNone, kValu, kGqaMfma, kMlaMfma };
 
+// KVD_PATH=valu restricts kernel selection to the general vector-ALU path
+// (for cross-checking the matrix-core kernels); anything else selects the
+// fastest kernel that handles the problem.
+bool valu_only() {
+  static const bool v = [] {
+    const char* e = std::getenv("KVD_PATH");
+    return e != nullptr && std::strcmp(e, "valu") == 0;
+  }();
+  return v;
+}
+
 Path choose(const kvd::PartialArgs& a) {
-  if (kvd::mla_mfma_supports(a)) return Path::kMlaMfma;
-  if (kvd::gqa_mfma_supports(a)) return Path::kGqaMfma;
+  if (!valu_only()) {
+    if (kvd::mla_mfma_supports(a)) return Path::kMlaMfma;
+    if (kvd::gqa_mfma_supports(a)) return Path::kGqaMfma;
+  }
   if (kvd::valu_supports(a)) return Path::kValu;
   return Path::kNone;
 }

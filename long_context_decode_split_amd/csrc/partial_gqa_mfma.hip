@@ -1,11 +1,428 @@
-// Split-KV partial attention for GQA groups on MFMA (to be filled in).
+// Split-KV partial attention for a GQA group of 16 query heads on MFMA.
+//
+// With 16 query heads sharing one KV head, every cached K and V element feeds
+// 16 multiply-adds, which is more arithmetic per HBM byte than the fp32 vector
+// ALUs can sustain for fp8 or MXFP4 caches.  The 16 heads of the group are
+// exactly the 16-wide dimension of the gfx950 bf16 matrix instruction
+// v_mfma_f32_16x16x32_bf16, so both contractions run on it:
+//
+//   S^T[token, head] = K_tile[token, :] . Q[head, :]          (K = 128 = 4 MFMAs)
+//   O^T[dv, head]   += V_tile^T[dv, token] . P^T[token, head] (32 tokens, 8 column
+//                                                              blocks x (hi, lo) = 16 MFMAs)
+//
+// Cache elements are decoded to bf16 in registers (bf16 as is; OCP E4M3 and
+// MXFP4 with the hardware converters, exactly) and Q is the bf16 query as
+// given, so the logits are exact products summed in fp32.  The softmax weights
+// P = exp2(logit - running max) are fp32; the PV product takes them as a bf16
+// pair hi + lo (two MFMAs), which keeps ~16 significant bits instead of 8, so
+// the output error stays near fp32 level even for short shards.
+//
+// Work split: one workgroup of 4 waves per (shard j, request b, KV head); wave
+// w takes the shard's 32-token tiles w, w+4, w+8, ... and loads the next tile
+// while computing the current one.  Lane (r, g) = (lane % 16, lane / 16):
+//  * K: lane (r, g) loads token r of each 16-token half-tile, bytes
+//    [64i + 16g, 64i + 16g + 16) of the row for each 16-byte load i, so each
+//    load instruction reads 64 contiguous bytes of 16 rows.
+//  * V: lane (r, g) loads columns [8r, 8r + 8) of the 8 tokens
+//    {4g..4g+3, 16+4g..16+4g+3}, one full row per 16 lanes per instruction, and
+//    regroups them with byte permutes into per-column token octets.
+//  * The S^T output of the MFMA gives lane (n, g) head n at tokens
+//    {4g+i, 16+4g+i}: exactly the P^T operand of the PV MFMA, so softmax state
+//    (running max, partial sum) is per lane and needs no transposes; the O^T
+//    accumulator of lane (n, g) is head n, dv in [32g, 32g + 32).
+// The running max is only moved when a tile's max exceeds it by more than 2^8
+// (in the exp2 domain); the stale max is exact algebra and keeps P <= 256.
+// At the end the four waves' (max, sum, acc) states are merged through LDS and
+// the normalized partial o and its natural-log lse are written.
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
 
 namespace kvd {
+namespace {
 
-bool gqa_mfma_supports(const PartialArgs&) { return false; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-hipError_t launch_partial_gqa_mfma(const PartialArgs&, hipStream_t) { return hipErrorInvalidValue; }
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kD = 128;        // head width (Dqk = Dv)
+constexpr int kTile = 32;      // tokens per wave iteration
+constexpr float kLazyMax = 8.0f;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4_t v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+  f32x2_t f = {x, y};
+  bf16x2_t h = __builtin_convertvector(f, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+template <int KV>
+struct Layout;
+
+// bf16: 64 B of K per lane per half-tile (4 loads), 16 B of V per token.
+template <>
+struct Layout<kBF16> {
+  static constexpr int kKLoads = 4;     // 16-byte K loads per lane per half-tile
+  static constexpr int kVBytes = 16;    // V bytes per lane per token
+  static constexpr int kRowBytes = 256;
+  // first d of MFMA chunk c for lane group g
+  __device__ static constexpr int chunk_d(int c, int g) { return 32 * c + 8 * g; }
+};
+template <>
+struct Layout<kFP8> {
+  static constexpr int kKLoads = 2;
+  static constexpr int kVBytes = 8;
+  static constexpr int kRowBytes = 128;
+  __device__ static constexpr int chunk_d(int c, int g) { return 64 * (c / 2) + 16 * g + 8 * (c % 2); }
+};
+template <>
+struct Layout<kMXFP4> {
+  static constexpr int kKLoads = 1;
+  static constexpr int kVBytes = 4;
+  static constexpr int kRowBytes = 64;
+  __device__ static constexpr int chunk_d(int c, int g) { return 32 * g + 8 * c; }
+};
+
+// Raw (undecoded) registers of one 32-token tile for one lane.
+template <int KV>
+struct Raw {
+  uint32_t k[2][Layout<KV>::kKLoads * 4];      // two half-tiles
+  uint32_t v[8][Layout<KV>::kVBytes / 4];      // 8 tokens
+  uint32_t ks[2];                              // MXFP4: K block exponent per half-tile
+  uint32_t vs[8];                              // MXFP4: V block exponent per token
+};
+
+template <int KV>
+__global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
+  using Lay = Layout<KV>;
+  constexpr int64_t ROW = Lay::kRowBytes;
+
+  __shared__ float sh_o[kWaves][16][kD + 4];
+  __shared__ float sh_m[kWaves][16];
+  __shared__ float sh_l[kWaves][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+
+  int flat = blockIdx.x;
+  const int kvh = flat % a.Hkv;
+  flat /= a.Hkv;
+  const int b = flat % a.B;
+  const int j = flat / a.B;
+
+  int64_t L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.S_max ? a.S_max : L);
+  int64_t s0, s1;
+  shard_range(L, a.kvp, j, &s0, &s1);
+  const int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
+
+  const int64_t slab = (int64_t)b * a.Hkv + kvh;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + slab * a.S_max * ROW;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + slab * a.S_max * ROW;
+  const uint8_t* ksbase = nullptr;
+  const uint8_t* vsbase = nullptr;
+  float kscale = 1.0f, vscale = 1.0f;
+  if constexpr (KV == kFP8) {
+    kscale = static_cast<const float*>(a.k_scale)[slab];
+    vscale = static_cast<const float*>(a.v_scale)[slab];
+  }
+  if constexpr (KV == kMXFP4) {
+    ksbase = static_cast<const uint8_t*>(a.k_scale) + slab * a.S_max * (kD / 32);
+    vsbase = static_cast<const uint8_t*>(a.v_scale) + slab * a.S_max * (kD / 32);
+  }
+  const float c2 = a.scale_log2 * kscale;  // raw logit -> log2 domain
+
+  // Q^T operand: lane (n, g) holds head n, the 8 d of chunk c for group g.
+  bf16x8_t qop[4];
+  {
+    const int h = kvh * 16 + r16;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h) * kD;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + Lay::chunk_d(c, g));
+      qop[c] = as_bf16x8(v.x, v.y, v.z, v.w);
+    }
+  }
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m2 = -INFINITY;  // running max of this lane's head (log2 domain)
+  float lsum = 0.0f;     // partial sum of P over this lane's tokens
+
+  const int64_t last = s1 - 1;
+  auto load = [&](Raw<KV>& rw, int tile) {
+    const int64_t base = s0 + (int64_t)tile * kTile;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int64_t t = base + 16 * u + r16;
+      t = t < last ? t : last;
+      const uint8_t* p = kbase + t * ROW + 16 * g;
+#pragma unroll
+      for (int i = 0; i < Lay::kKLoads; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p + 64 * i);
+        rw.k[u][4 * i + 0] = v.x;
+        rw.k[u][4 * i + 1] = v.y;
+        rw.k[u][4 * i + 2] = v.z;
+        rw.k[u][4 * i + 3] = v.w;
+      }
+      if constexpr (KV == kMXFP4) rw.ks[u] = ksbase[t * (kD / 32) + g];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int64_t t = base + 16 * (e / 4) + 4 * g + (e % 4);
+      t = t < last ? t : last;
+      const uint8_t* p = vbase + t * ROW + Lay::kVBytes * r16;
+      if constexpr (Lay::kVBytes == 16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        rw.v[e][0] = v.x;
+        rw.v[e][1] = v.y;
+        rw.v[e][2] = v.z;
+        rw.v[e][3] = v.w;
+      } else if constexpr (Lay::kVBytes == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        rw.v[e][0] = v.x;
+        rw.v[e][1] = v.y;
+      } else {
+        rw.v[e][0] = *reinterpret_cast<const uint32_t*>(p);
+      }
+      if constexpr (KV == kMXFP4) rw.vs[e] = vsbase[t * (kD / 32) + r16 / 4];
+    }
+  };
+
+  auto compute = [&](const Raw<KV>& rw, int tile) {
+    const int64_t base = s0 + (int64_t)tile * kTile;
+    // ---- logits S^T = K Q^T for the two half-tiles
+    f32x4_t s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      float ksc = 1.0f;
+      if constexpr (KV == kMXFP4) ksc = e8m0_to_f32(rw.ks[u]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x8_t kop;
+        if constexpr (KV == kBF16) {
+          kop = as_bf16x8(rw.k[u][4 * c], rw.k[u][4 * c + 1], rw.k[u][4 * c + 2], rw.k[u][4 * c + 3]);
+        } else if constexpr (KV == kFP8) {
+          const uint32_t w0 = rw.k[u][2 * c], w1 = rw.k[u][2 * c + 1];
+          kop = __builtin_bit_cast(
+              bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))});
+        } else {
+          const uint32_t w = rw.k[u][c];
+          kop = __builtin_bit_cast(
+              bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 0)),
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 1)),
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 2)),
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 3))});
+        }
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[c], s[u], 0, 0, 0);
+      }
+    }
+    // ---- online softmax for head n = r16 over tokens base + 16u + 4g + i
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = base + 16 * u + 4 * g + i;
+        x[4 * u + i] = (t < s1) ? s[u][i] : -INFINITY;
+      }
+    }
+    float tmax = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float tmax2 = tmax * c2;
+    if (__any(tmax2 > m2 + kLazyMax)) {
+      const float mn = fmaxf(m2, tmax2);
+      const float al = fast_exp2(m2 - mn);
+      lsum *= al;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= al;
+      m2 = mn;
+    }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = fast_exp2(fmaf(x[e], c2, -m2));
+      p[e] = (x[e] == -INFINITY) ? 0.0f : pe;
+      lsum += p[e];
+    }
+    // P = hi + lo: hi keeps the upper 16 bits of each fp32 weight (exact), lo
+    // is the remainder rounded to bf16, so hi + lo carries ~16 significant bits.
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const uint32_t b0 = __float_as_uint(p[2 * rr]), b1 = __float_as_uint(p[2 * rr + 1]);
+      ph[rr] = perm(b1, b0, 0x07060302u);
+      pl[rr] = pack_bf16(p[2 * rr] - __uint_as_float(b0 & 0xFFFF0000u),
+                         p[2 * rr + 1] - __uint_as_float(b1 & 0xFFFF0000u));
+    }
+    const bf16x8_t pop = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
+    const bf16x8_t pol = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+    // ---- O^T += V^T P^T, one MFMA per 16-column block (column 8*r16 + blk)
+    if constexpr (KV == kBF16 || KV == kMXFP4) {
+      // token-major bf16 pairs cv[e][q] = columns (8 r16 + 2q, 8 r16 + 2q + 1) of token e
+      uint32_t cv[8][4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (KV == kBF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cv[e][q] = rw.v[e][q];
+        } else {
+          const float vsc = e8m0_to_f32(rw.vs[e]);
+          const uint32_t w = rw.v[e][0];
+          cv[e][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 0));
+          cv[e][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 1));
+          cv[e][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 2));
+          cv[e][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 3));
+        }
+      }
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const int q = blk / 2;
+        const uint32_t sel = (blk & 1) ? 0x07060302u : 0x05040100u;
+        const bf16x8_t vop = as_bf16x8(perm(cv[1][q], cv[0][q], sel), perm(cv[3][q], cv[2][q], sel),
+                                       perm(cv[5][q], cv[4][q], sel), perm(cv[7][q], cv[6][q], sel));
+        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[blk], 0, 0, 0);
+        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pol, acc[blk], 0, 0, 0);
+      }
+    } else {
+      // fp8: interleave bytes of token pairs, then convert both halves
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; s2 += 2) {
+          const uint32_t sel = (s2 == 0) ? 0x05010400u : 0x07030602u;
+          uint32_t lo[4], hi[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t x2 = perm(rw.v[2 * rr + 1][q], rw.v[2 * rr][q], sel);
+            lo[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, false));
+            hi[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, true));
+          }
+          const int blk = 4 * q + s2;
+          const bf16x8_t va = as_bf16x8(lo[0], lo[1], lo[2], lo[3]);
+          const bf16x8_t vb = as_bf16x8(hi[0], hi[1], hi[2], hi[3]);
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, acc[blk], 0, 0, 0);
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pol, acc[blk], 0, 0, 0);
+          acc[blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pop, acc[blk + 1], 0, 0, 0);
+          acc[blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pol, acc[blk + 1], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Double-buffered stream over this wave's tiles.  The next tile is always
+  // loaded (rows clamped into the shard), so the waits stay static.
+  if (ntiles > 0) {
+    Raw<KV> ra, rb;
+    int tile = wave;
+    load(ra, tile < ntiles ? tile : ntiles - 1);
+    while (tile < ntiles) {
+      const int nx = tile + kWaves;
+      load(rb, nx < ntiles ? nx : ntiles - 1);
+      compute(ra, tile);
+      tile = nx;
+      if (tile >= ntiles) break;
+      const int nx2 = tile + kWaves;
+      load(ra, nx2 < ntiles ? nx2 : ntiles - 1);
+      compute(rb, tile);
+      tile = nx2;
+    }
+  }
+
+  // ---- merge the four waves and write the partial
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh_o[wave][r16][32 * g + 8 * i + blk] = acc[blk][i];
+  }
+  if (g == 0) {
+    sh_m[wave][r16] = m2;
+    sh_l[wave][r16] = lsum;
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < 16 * kD; idx += kThreads) {
+    const int n = idx / kD;
+    const int d = idx - n * kD;
+    float M = sh_m[0][n];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][n]);
+    float o = 0.0f;
+    if (M != -INFINITY) {
+      float lt = 0.0f, ot = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = rescale_weight(sh_m[w][n], M);
+        lt += sh_l[w][n] * f;
+        ot += sh_o[w][n][d] * f;
+      }
+      o = ot / lt * vscale;
+    }
+    a.o_part[(((int64_t)j * a.B + b) * a.Hq + kvh * 16 + n) * kD + d] = o;
+  }
+  if (tid < 16) {
+    float M = sh_m[0][tid];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][tid]);
+    float lse = -INFINITY;
+    if (M != -INFINITY) {
+      float lt = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) lt += sh_l[w][tid] * rescale_weight(sh_m[w][tid], M);
+      lse = (M + fast_log2(lt)) * kLn2;
+    }
+    a.lse_part[((int64_t)j * a.B + b) * a.Hq + kvh * 16 + tid] = lse;
+  }
+}
+
+}  // namespace
+
+bool gqa_mfma_supports(const PartialArgs& a) {
+  if (!a.q_bf16 || a.v_aliases_k) return false;
+  if (a.Dqk != kD || a.Dv != kD) return false;
+  if (a.Hq / a.Hkv != 16) return false;
+  return a.kv_format == kBF16 || a.kv_format == kFP8 || a.kv_format == kMXFP4;
+}
+
+hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.kvp * a.B * a.Hkv;
+  switch (a.kv_format) {
+    case kBF16:
+      hipLaunchKernelGGL(gqa_mfma_kernel<kBF16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      break;
+    case kFP8:
+      hipLaunchKernelGGL(gqa_mfma_kernel<kFP8>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      break;
+    case kMXFP4:
+      hipLaunchKernelGGL(gqa_mfma_kernel<kMXFP4>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 }  // namespace kvd
