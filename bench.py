@@ -31,10 +31,24 @@ if HERE not in sys.path:
 
 METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S=1M GQA"
 
-# HBM bytes per launch of the partial kernel measured with rocprofv3 counters,
-# keyed by (workload, kvp, kernel revision); see profiles/.
-TRAFFIC = {}
-KERNEL_REVISION = "valu-1"
+# HBM bytes per launch of the partial kernel measured with rocprofv3 counters
+# (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a plain 1 GiB
+# copy), keyed by (workload, kvp, sha256 prefix of the kernel source the
+# counters were taken on).  A changed kernel source no longer matches, and the
+# bench then reports traffic as null.  Summaries are under profiles/.
+TRAFFIC = {
+    ("helix_fp8", 32, "71b1b280f079ac15"): 17207578650,
+}
+KERNEL_SOURCES = {"bf16": "partial_gqa_mfma.hip", "fp8": "partial_gqa_mfma.hip",
+                  "mxfp4": "partial_gqa_mfma.hip", "f32": "partial_valu.hip"}
+
+
+def kernel_hash(kv_dtype, mla=False):
+    import hashlib
+    name = "partial_mla_mfma.hip" if mla else KERNEL_SOURCES[kv_dtype]
+    path = os.path.join(HERE, "long_context_decode_split_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def log(msg):
@@ -97,6 +111,9 @@ def main():
     ap.add_argument("--kvp", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 5 times (the "
+                         "reference kernel for scaling HBM byte counters), and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -105,6 +122,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration, "launches": 5}))
+        return
 
     import kvgen
     from kvgen.device import generate_on_device
@@ -163,7 +189,8 @@ def main():
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (partial_avg * 1e-3) / 1e9
     peak = roofline.HBM_BYTES_PER_S / 1e9
-    traffic = TRAFFIC.get((w.name, kvp, KERNEL_REVISION))
+    khash = kernel_hash(w.kv_dtype, mla=w.v_aliases_k)
+    traffic = TRAFFIC.get((w.name, kvp, khash))
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -177,7 +204,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if w.kv_dtype == "f32" else "bf16",
+        "arith": "f32 vector ALU" if w.kv_dtype == "f32" else
+                 "bf16 MFMA on exactly decoded %s cache, fp32 accumulate and softmax" % w.kv_dtype,
         "data": "synthetic (seeded N(0,1), encoded to the cache format)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Hsz": w.Dqk, "Dv": w.Dv,
                    "S": w.S_max, "kvp": kvp, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
@@ -186,7 +215,8 @@ def main():
         "merge_us": round(sum(merge_ms) / len(merge_ms) * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": peak, "unit": "GB/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "kvd partial pass", "bytes_per_launch": kv_bytes,
+                     "kernel": "kvd partial pass", "kernel_source_hash": khash,
+                     "bytes_per_launch": kv_bytes,
                      "tflops": round(flops / (partial_avg * 1e-3) / 1e12, 2)},
     }
     del dev
