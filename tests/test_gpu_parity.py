@@ -84,6 +84,60 @@ def test_v_aliases_k_square():
     gc.check_full(w, 3)
 
 
+def test_mla_small():
+    """Latent heads (128 per KV head, Dqk=576, V = first 512 columns of K), ragged and empty."""
+    for kvh, seq in ((1, (300, 17, 0)), (2, (77, 300, 33))):
+        w = W("mla_small_%d" % kvh, B=3, Hq=128 * kvh, Hkv=kvh, Dqk=576, Dv=512, S_max=300,
+              seq_lens=seq, kv_dtype="bf16", v_aliases_k=True, seed=31 + kvh)
+        for kvp in (1, 3, 16):
+            gc.check_full(w, kvp)
+
+
+def _ramp_inputs(w, growth):
+    """Planted inputs whose logits grow along the sequence: every cached key
+    is (t + 1) times one direction u and every query is a multiple of u, so the
+    running max keeps rising by `growth` (in natural-log units) per token."""
+    import numpy as np
+    inp = kvgen.make_inputs(w)
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal(w.Dqk)
+    u /= np.linalg.norm(u)
+    sm = 1.0 / np.sqrt(w.Dqk)
+    t = np.arange(w.S_max, dtype=np.float64)
+    k = (t[:, None] + 1.0) * u[None, :] * 0.05
+    qv = u * growth / (sm * 0.05)
+    def bf16(x):
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    inp.k_data[...] = bf16(k)[None, None]
+    inp.q[...] = bf16(np.broadcast_to(qv, inp.q.shape))
+    return inp
+
+
+@pytest.mark.parametrize("kind", ["gqa", "mla"])
+def test_rising_logits(kind):
+    """Logits that rise by ~0.3 nats per token (hundreds of nats per shard)
+    exercise the running-max updates of the GQA kernel and the restart pass of
+    the latent kernel; the result is dominated by the last tokens."""
+    from kvgen.device import upload
+    import oracle
+    if kind == "gqa":
+        w = W("ramp_gqa", B=1, Hq=16, Hkv=1, S_max=700, seq_lens=(700,), kv_dtype="bf16")
+    else:
+        w = W("ramp_mla", B=1, Hq=128, Hkv=1, Dqk=576, Dv=512, S_max=700, seq_lens=(700,),
+              kv_dtype="bf16", v_aliases_k=True)
+    inp = _ramp_inputs(w, 0.3)
+    dev = upload(inp)
+    for kvp in (1, 4):
+        o_part, lse_part, o, lse = gc.run_library(dev, kvp)
+        p = oracle.Problem.from_workload(w)
+        args = (inp.q, inp.k_data, inp.k_scale, inp.v_data, inp.v_scale, inp.seq_lens)
+        ref_po, ref_pl = oracle.decode_partials(p, kvp, *args)
+        ref_o, ref_l = oracle.decode(p, *args)
+        gc.compare(o_part, lse_part, ref_po, ref_pl, w.kv_dtype, "%s ramp kvp=%d partials" % (kind, kvp))
+        gc.compare(o, lse, ref_o, ref_l, w.kv_dtype, "%s ramp kvp=%d merged" % (kind, kvp))
+
+
 def test_repeat_runs_bitwise_identical():
     from kvgen.device import upload
     w = W("det", kv_dtype="fp8", S_max=2000, seq_lens=(2000, 1999, 1000))
