@@ -35,26 +35,46 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
   return s;
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) loads of cache bytes.  Every cached byte is read
+// once per call, so the loads carry the non-temporal hint; on MI355X this is
+// what lets a read stream approach HBM peak (regular loads plateau ~10%
+// lower).  p must be aligned to the access size.
+__device__ __forceinline__ u32x4_t stream_load16(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ u32x2_t stream_load8(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+__device__ __forceinline__ uint32_t stream_load4(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ uint32_t stream_load1(const uint8_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // Load N bytes (N in {4, 8, 16, 32, 64}) from a 4-byte-aligned (N >= 16:
-// 16-byte aligned) global address into N/4 dwords.
+// 16-byte aligned) global address into N/4 dwords, streaming.
 template <int N>
 __device__ __forceinline__ void load_dwords(const uint8_t* __restrict__ p, uint32_t* w) {
   static_assert(N % 4 == 0 && N >= 4, "whole dwords only");
   if constexpr (N >= 16) {
 #pragma unroll
     for (int i = 0; i < N / 16; ++i) {
-      uint4 v = *reinterpret_cast<const uint4*>(p + 16 * i);
-      w[4 * i + 0] = v.x;
-      w[4 * i + 1] = v.y;
-      w[4 * i + 2] = v.z;
-      w[4 * i + 3] = v.w;
+      const u32x4_t v = stream_load16(p + 16 * i);
+      w[4 * i + 0] = v[0];
+      w[4 * i + 1] = v[1];
+      w[4 * i + 2] = v[2];
+      w[4 * i + 3] = v[3];
     }
   } else if constexpr (N == 8) {
-    uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x;
-    w[1] = v.y;
+    const u32x2_t v = stream_load8(p);
+    w[0] = v[0];
+    w[1] = v[1];
   } else {
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    w[0] = stream_load4(p);
   }
 }
 

@@ -44,7 +44,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -173,13 +172,13 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       const uint8_t* p = kbase + t * ROW + 16 * g;
 #pragma unroll
       for (int i = 0; i < Lay::kKLoads; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p + 64 * i);
-        rw.k[u][4 * i + 0] = v.x;
-        rw.k[u][4 * i + 1] = v.y;
-        rw.k[u][4 * i + 2] = v.z;
-        rw.k[u][4 * i + 3] = v.w;
+        const u32x4_t v = stream_load16(p + 64 * i);
+        rw.k[u][4 * i + 0] = v[0];
+        rw.k[u][4 * i + 1] = v[1];
+        rw.k[u][4 * i + 2] = v[2];
+        rw.k[u][4 * i + 3] = v[3];
       }
-      if constexpr (KV == kMXFP4) rw.ks[u] = ksbase[t * (kD / 32) + g];
+      if constexpr (KV == kMXFP4) rw.ks[u] = stream_load1(ksbase + t * (kD / 32) + g);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -187,19 +186,19 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       t = t < last ? t : last;
       const uint8_t* p = vbase + t * ROW + Lay::kVBytes * r16;
       if constexpr (Lay::kVBytes == 16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
-        rw.v[e][0] = v.x;
-        rw.v[e][1] = v.y;
-        rw.v[e][2] = v.z;
-        rw.v[e][3] = v.w;
+        const u32x4_t v = stream_load16(p);
+        rw.v[e][0] = v[0];
+        rw.v[e][1] = v[1];
+        rw.v[e][2] = v[2];
+        rw.v[e][3] = v[3];
       } else if constexpr (Lay::kVBytes == 8) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        rw.v[e][0] = v.x;
-        rw.v[e][1] = v.y;
+        const u32x2_t v = stream_load8(p);
+        rw.v[e][0] = v[0];
+        rw.v[e][1] = v[1];
       } else {
-        rw.v[e][0] = *reinterpret_cast<const uint32_t*>(p);
+        rw.v[e][0] = stream_load4(p);
       }
-      if constexpr (KV == kMXFP4) rw.vs[e] = vsbase[t * (kD / 32) + r16 / 4];
+      if constexpr (KV == kMXFP4) rw.vs[e] = stream_load1(vsbase + t * (kD / 32) + r16 / 4);
     }
   };
 

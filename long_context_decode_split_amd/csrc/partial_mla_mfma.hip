@@ -40,7 +40,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -123,7 +122,8 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   // LDS byte address of the dynamic buffer ring.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)smem;
 
-  // Issue the direct-to-LDS loads of tile `tile` into buffer `buf`.  They are
+  // Issue the direct-to-LDS loads of tile `tile` into buffer `buf` (with the
+  // non-temporal hint: every cached byte is read once).  They are
   // written as inline asm so that the compiler does not treat every later LDS
   // read as possibly aliasing them (it would wait for all of them, including
   // the prefetch of the next tiles); the waits are explicit below.
@@ -146,10 +146,17 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
       // M0 = LDS byte address of this wave's 64 consecutive slots
       const uint32_t dst = __builtin_amdgcn_readfirstlane(
           lds0 + (uint32_t)(buf * (kSlots * 16) + (k * kThreads + wave * 64) * 16));
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :
-                   : "s"(dst), "v"(src)
-                   : "memory", "m0");
+      // (M0 is saved and restored around the load: the compiler owns it)
+      uint32_t m0_saved;
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %2, off nt\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(m0_saved)
+          : "s"(dst), "v"(src)
+          : "memory");
     }
   };
 

@@ -139,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
     load_dwords<KLANE>(kp + t * KROW, kw);
     load_dwords<VLANE>(vp + t * VROW, vw);
     if constexpr (KV == kMXFP4) {
-      *ks = e8m0_to_f32(ksp[t * KSROW]);
-      *vs = e8m0_to_f32(vsp[t * VSROW]);
+      *ks = e8m0_to_f32(stream_load1(ksp + t * KSROW));
+      *vs = e8m0_to_f32(stream_load1(vsp + t * VSROW));
     } else {
       *ks = 1.0f;
       *vs = 1.0f;
