@@ -23,6 +23,13 @@ ARCH = "gfx950"
 SOURCES = ["api.cpp", "lse_merge.hip", "partial_valu.hip", "partial_gqa_mfma.hip",
            "partial_mla_mfma.hip"]
 
+# Per-source extra flags.  The GQA kernel keeps its MFMA accumulators in
+# ordinary VGPRs (it has room, and the occasional vector-ALU rescale of the
+# accumulator would otherwise make the compiler shuttle them between AGPRs
+# and VGPRs every tile); the latent kernel needs all 256 AGPRs for its
+# accumulator and keeps the default.
+SOURCE_FLAGS = {"partial_gqa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -31,7 +38,7 @@ CFLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + SOURCE_FLAGS.get(src, []) + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(line for line in r.stdout.splitlines() if "packed-fp32-ops" not in line
                     and "not a recognized feature" not in line)

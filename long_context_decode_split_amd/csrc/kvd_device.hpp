@@ -35,6 +35,12 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
   return s;
 }
 
+// E8M0 -> fp32 as a bare exponent shift, for the matrix-core kernels: exact
+// for E in [1, 254]; E = 0 gives 0 instead of 2^-127 (every element of such a
+// block is below 6 * 2^-127, under fp32's normal range) and E = 255 (NaN)
+// gives +inf, so a NaN block scale yields non-finite results.
+__device__ __forceinline__ float e8m0_to_f32_fast(uint32_t e) { return __uint_as_float(e << 23); }
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 

@@ -18,8 +18,10 @@
 // the output error stays near fp32 level even for short shards.
 //
 // Work split: one workgroup of 4 waves per (shard j, request b, KV head); wave
-// w takes the shard's 32-token tiles w, w+4, w+8, ... and loads the next tile
-// while computing the current one.  Lane (r, g) = (lane % 16, lane / 16):
+// w takes the shard's 32-token tiles w, w+4, w+8, ... and keeps the loads of
+// its next one (bf16) or two (fp8, MXFP4: smaller tiles) tiles in flight while
+// computing the current one, so enough bytes are outstanding to cover HBM
+// latency at 2 waves per SIMD.  Lane (r, g) = (lane % 16, lane / 16):
 //  * K: lane (r, g) loads token r of each 16-token half-tile, bytes
 //    [64i + 16g, 64i + 16g + 16) of the row for each 16-byte load i, so each
 //    load instruction reads 64 contiguous bytes of 16 rows.
@@ -34,6 +36,8 @@
 // (in the exp2 domain); the stale max is exact algebra and keeps P <= 256.
 // At the end the four waves' (max, sum, acc) states are merged through LDS and
 // the normalized partial o and its natural-log lse are written.
+#include <type_traits>
+
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
 
@@ -72,6 +76,7 @@ struct Layout;
 // bf16: 64 B of K per lane per half-tile (4 loads), 16 B of V per token.
 template <>
 struct Layout<kBF16> {
+  static constexpr int kRing = 2;       // tiles held in registers (current + prefetched)
   static constexpr int kKLoads = 4;     // 16-byte K loads per lane per half-tile
   static constexpr int kVBytes = 16;    // V bytes per lane per token
   static constexpr int kRowBytes = 256;
@@ -80,6 +85,7 @@ struct Layout<kBF16> {
 };
 template <>
 struct Layout<kFP8> {
+  static constexpr int kRing = 3;
   static constexpr int kKLoads = 2;
   static constexpr int kVBytes = 8;
   static constexpr int kRowBytes = 128;
@@ -87,6 +93,7 @@ struct Layout<kFP8> {
 };
 template <>
 struct Layout<kMXFP4> {
+  static constexpr int kRing = 3;
   static constexpr int kKLoads = 1;
   static constexpr int kVBytes = 4;
   static constexpr int kRowBytes = 64;
@@ -112,7 +119,8 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   __shared__ float sh_l[kWaves][16];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar, so everything derived from it stays wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
@@ -163,13 +171,30 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   float lsum = 0.0f;     // partial sum of P over this lane's tokens
 
   const int64_t last = s1 - 1;
-  auto load = [&](Raw<KV>& rw, int tile) {
+  // Per-lane byte offsets inside a tile (loop invariant, 32-bit): a full tile
+  // is addressed as (wave-uniform tile pointer) + (lane offset) + (immediate),
+  // which needs no per-load vector arithmetic.
+  const uint32_t koff = (uint32_t)(r16 * ROW + 16 * g);
+  const uint32_t voff = (uint32_t)(4 * g * ROW + Lay::kVBytes * r16);
+  const uint32_t ksoff = (uint32_t)(r16 * (kD / 32) + g);
+  const uint32_t vsoff = (uint32_t)(4 * g * (kD / 32) + r16 / 4);
+
+  // FULL: every row of the tile is inside the shard (no clamping needed).
+  auto load = [&](Raw<KV>& rw, int tile, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int64_t base = s0 + (int64_t)tile * kTile;
+    const uint8_t* kt = kbase + base * ROW;
+    const uint8_t* vt = vbase + base * ROW;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      int64_t t = base + 16 * u + r16;
-      t = t < last ? t : last;
-      const uint8_t* p = kbase + t * ROW + 16 * g;
+      const uint8_t* p;
+      if constexpr (FULL) {
+        p = kt + koff + 16 * u * ROW;
+      } else {
+        int64_t t = base + 16 * u + r16;
+        t = t < last ? t : last;
+        p = kbase + t * ROW + 16 * g;
+      }
 #pragma unroll
       for (int i = 0; i < Lay::kKLoads; ++i) {
         const u32x4_t v = stream_load16(p + 64 * i);
@@ -178,13 +203,30 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
         rw.k[u][4 * i + 2] = v[2];
         rw.k[u][4 * i + 3] = v[3];
       }
-      if constexpr (KV == kMXFP4) rw.ks[u] = stream_load1(ksbase + t * (kD / 32) + g);
+      if constexpr (KV == kMXFP4) {
+        if constexpr (FULL) {
+          rw.ks[u] = stream_load1(ksbase + base * (kD / 32) + ksoff + 16 * u * (kD / 32));
+        } else {
+          int64_t t = base + 16 * u + r16;
+          t = t < last ? t : last;
+          rw.ks[u] = stream_load1(ksbase + t * (kD / 32) + g);
+        }
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      int64_t t = base + 16 * (e / 4) + 4 * g + (e % 4);
-      t = t < last ? t : last;
-      const uint8_t* p = vbase + t * ROW + Lay::kVBytes * r16;
+      const int erow = 16 * (e / 4) + (e % 4);   // row of token e relative to 4g
+      const uint8_t* p;
+      const uint8_t* ps = nullptr;
+      if constexpr (FULL) {
+        p = vt + voff + erow * ROW;
+        if constexpr (KV == kMXFP4) ps = vsbase + base * (kD / 32) + vsoff + erow * (kD / 32);
+      } else {
+        int64_t t = base + erow + 4 * g;
+        t = t < last ? t : last;
+        p = vbase + t * ROW + Lay::kVBytes * r16;
+        if constexpr (KV == kMXFP4) ps = vsbase + t * (kD / 32) + r16 / 4;
+      }
       if constexpr (Lay::kVBytes == 16) {
         const u32x4_t v = stream_load16(p);
         rw.v[e][0] = v[0];
@@ -198,11 +240,13 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       } else {
         rw.v[e][0] = stream_load4(p);
       }
-      if constexpr (KV == kMXFP4) rw.vs[e] = stream_load1(vsbase + t * (kD / 32) + r16 / 4);
+      if constexpr (KV == kMXFP4) rw.vs[e] = stream_load1(ps);
     }
   };
 
-  auto compute = [&](const Raw<KV>& rw, int tile) {
+  // MASK: the tile runs past the shard end; its extra tokens get zero weight.
+  auto compute = [&](const Raw<KV>& rw, int tile, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int64_t base = s0 + (int64_t)tile * kTile;
     // ---- logits S^T = K Q^T for the two half-tiles
     f32x4_t s[2];
@@ -210,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     for (int u = 0; u < 2; ++u) {
       s[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       float ksc = 1.0f;
-      if constexpr (KV == kMXFP4) ksc = e8m0_to_f32(rw.ks[u]);
+      if constexpr (KV == kMXFP4) ksc = e8m0_to_f32_fast(rw.ks[u]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         bf16x8_t kop;
@@ -237,12 +281,16 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     // ---- online softmax for head n = r16 over tokens base + 16u + 4g + i
     float x[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = base + 16 * u + 4 * g + i;
-        x[4 * u + i] = (t < s1) ? s[u][i] : -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i) x[4 * u + i] = s[u][i];
+    if constexpr (MASK) {
+      const int nvalid = (int)(s1 - base);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * u + 4 * g + i >= nvalid) x[4 * u + i] = -INFINITY;
     }
     float tmax = x[0];
 #pragma unroll
@@ -261,8 +309,8 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(fmaf(x[e], c2, -m2));
-      p[e] = (x[e] == -INFINITY) ? 0.0f : pe;
+      p[e] = fast_exp2(fmaf(x[e], c2, -m2));
+      if constexpr (MASK) p[e] = (x[e] == -INFINITY) ? 0.0f : p[e];
       lsum += p[e];
     }
     // P = hi + lo: hi keeps the upper 16 bits of each fp32 weight (exact), lo
@@ -287,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) cv[e][q] = rw.v[e][q];
         } else {
-          const float vsc = e8m0_to_f32(rw.vs[e]);
+          const float vsc = e8m0_to_f32_fast(rw.vs[e]);
           const uint32_t w = rw.v[e][0];
           cv[e][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 0));
           cv[e][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 1));
@@ -330,23 +378,52 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     }
   };
 
-  // Double-buffered stream over this wave's tiles.  The next tile is always
-  // loaded (rows clamped into the shard), so the waits stay static.
-  if (ntiles > 0) {
-    Raw<KV> ra, rb;
+  // Stream over this wave's full tiles with kRing register buffers: the loads
+  // of the next kRing-1 tiles are in flight while a tile is computed.  The
+  // next loads are always issued (clamped to the last full tile) so the waits
+  // stay static.  A partial last tile is handled once, after the ring.
+  using Full = std::true_type;
+  using Part = std::false_type;
+  const int nfull = (int)((s1 - s0) / kTile);
+  if (nfull > 0) {
+    auto clampt = [&](int t) { return t < nfull - 1 ? t : nfull - 1; };
     int tile = wave;
-    load(ra, tile < ntiles ? tile : ntiles - 1);
-    while (tile < ntiles) {
-      const int nx = tile + kWaves;
-      load(rb, nx < ntiles ? nx : ntiles - 1);
-      compute(ra, tile);
-      tile = nx;
-      if (tile >= ntiles) break;
-      const int nx2 = tile + kWaves;
-      load(ra, nx2 < ntiles ? nx2 : ntiles - 1);
-      compute(rb, tile);
-      tile = nx2;
+    if constexpr (Lay::kRing == 2) {
+      Raw<KV> ra, rb;
+      load(ra, clampt(tile), Full{});
+      while (tile < nfull) {
+        load(rb, clampt(tile + kWaves), Full{});
+        compute(ra, tile, Part{});
+        tile += kWaves;
+        if (tile >= nfull) break;
+        load(ra, clampt(tile + kWaves), Full{});
+        compute(rb, tile, Part{});
+        tile += kWaves;
+      }
+    } else {
+      static_assert(Lay::kRing == 3, "ring of 2 or 3 buffers");
+      Raw<KV> ra, rb, rc;
+      load(ra, clampt(tile), Full{});
+      load(rb, clampt(tile + kWaves), Full{});
+      while (tile < nfull) {
+        load(rc, clampt(tile + 2 * kWaves), Full{});
+        compute(ra, tile, Part{});
+        tile += kWaves;
+        if (tile >= nfull) break;
+        load(ra, clampt(tile + 2 * kWaves), Full{});
+        compute(rb, tile, Part{});
+        tile += kWaves;
+        if (tile >= nfull) break;
+        load(rb, clampt(tile + 2 * kWaves), Full{});
+        compute(rc, tile, Part{});
+        tile += kWaves;
+      }
     }
+  }
+  if (nfull < ntiles && nfull % kWaves == wave) {
+    Raw<KV> rt;
+    load(rt, nfull, Part{});
+    compute(rt, nfull, Full{});
   }
 
   // ---- merge the four waves and write the partial

@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar, so everything derived from it stays wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
