@@ -155,6 +155,23 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48), on the
+// gfx950 row-swap permutes: swapping a value with itself between row pairs
+// leaves each lane holding one value of each pair in the two results, so
+// op(first, second) is the pairwise reduction, identical in both rows.
+__device__ __forceinline__ float rows4_max(float v) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -295,9 +295,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     float tmax = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float tmax2 = tmax * c2;
+    const float tmax2 = rows4_max(tmax) * c2;
     if (__any(tmax2 > m2 + kLazyMax)) {
       const float mn = fmaxf(m2, tmax2);
       const float al = fast_exp2(m2 - mn);
@@ -427,8 +425,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   }
 
   // ---- merge the four waves and write the partial
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = rows4_sum(lsum);
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
 #pragma unroll

@@ -20,16 +20,21 @@
 // rate at the HBM roof.
 //
 // Tiles travel HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a
-// ring of kBufs buffers, two tiles ahead.  Inside a buffer a tile row occupies
-// 73 16-byte slots (1168 B: the 1152-byte row plus one pad slot), so 16 rows
-// read at the same column start in 16 different bank groups, and every LDS
-// read address is a per-lane base plus a compile-time offset.  Each
-// wave-instruction of the loads fills 64 consecutive slots; lanes that land on
-// a pad slot (or on the spare slots that round the tile up to 10 loads per
-// thread) load a harmless in-shard chunk.  K operands are ds_read_b128 of 8
-// contiguous dims of one token; V^T operands come from ds_read_b64_tr_b16,
-// whose 16-lane transpose turns four 16-column row segments into one column of
-// 4 tokens per lane, which is exactly the V^T MFMA operand.
+// ring of kBufs buffers, two tiles ahead.  A buffer has two regions: the first
+// 1024 bytes of each of the 32 rows (dims 0..511) at a stride of 65 16-byte
+// slots, one row per load instruction, and the last 128 bytes (dims 512..575)
+// at a stride of 9 slots, four rows per load instruction.  Every source
+// address is a wave-uniform row pointer plus a fixed lane offset.
+//
+// Within each 16-token half-tile, MFMA row m holds token perm16(m), which
+// interleaves even and odd tokens so that the LDS reads are free of bank
+// conflicts: the 8 rows read together by a ds_read_b128 of K fall on 8
+// different 16-byte bank groups (strides 65 and 9 are 1 mod 8), and the four
+// rows read by each 16-lane ds_read_b64_tr_b16 group of V are two apart, 8
+// banks from each other.  K operands are ds_read_b128 of 8 contiguous dims of
+// one token; V^T operands come from ds_read_b64_tr_b16, whose 16-lane
+// transpose turns four 16-column row segments into one column of 4 tokens per
+// lane, which is exactly the V^T MFMA operand.
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
 
@@ -45,20 +50,21 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kHeads = 128;           // query heads per KV head
+constexpr int kHeads = 128;                 // query heads per KV head
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
-constexpr int kRowBytes = kDqk * 2;   // 1152
-constexpr int kChunks = kRowBytes / 16;  // 72 16-byte chunks per row
-constexpr int kStride = kChunks + 1;     // 73 slots per row in LDS
+constexpr int kRowBytes = kDqk * 2;         // 1152
+constexpr int kMainRowBytes = 1024;         // dims 0..511: one load instruction per row
 constexpr int kTile = 32;
-constexpr int kUsed = kTile * kStride;   // 2336 slots hold the tile
-constexpr int kLoads = 10;               // direct-to-LDS loads per thread per tile
-constexpr int kSlots = kLoads * kThreads;  // 2560 slots (40 KB) per buffer
+constexpr int kRowsPerWave = kTile / kWaves;
+constexpr int kMainStride = 65;             // 16-byte slots per row, dims 0..511 (+1 pad)
+constexpr int kTailStride = 9;              // 16-byte slots per row, dims 512..575 (+1 pad)
+constexpr int kMainBytes = kTile * kMainStride * 16;   // 33280
+constexpr int kTailBytes = kTile * kTailStride * 16;   // 4608
+constexpr int kBufBytes = kMainBytes + kTailBytes;     // 37888
 constexpr int kBufs = 3;
+constexpr int kLoads = kRowsPerWave + kRowsPerWave / 4;  // load instructions per wave per tile
 constexpr float kHeadroom = 64.0f;  // max log2 growth of P over the reference
-
-static_assert(kSlots >= kUsed, "buffer must hold the tile");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4_t v = {a, b, c, d};
@@ -71,6 +77,28 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Token (within a 16-token half-tile) held by MFMA row m = 4a + i:
+// a = 0 -> 0,2,4,6; a = 1 -> 1,3,5,7; a = 2 -> 8,..,14; a = 3 -> 9,..,15.
+__device__ __forceinline__ int perm16(int m) { return ((m >> 2) & 1) + 2 * (m & 3) + 8 * (m >> 3); }
+
+// One direct-to-LDS 16-byte load per active lane: global address sbase + voff
+// into LDS address M0 + 16 * lane, with the non-temporal hint (every cached
+// byte is read once).  Inline asm, so the compiler does not take later LDS
+// reads as aliasing it (it would wait for every load in flight, including the
+// prefetch of the next tiles); the waits are explicit.  M0 belongs to the
+// compiler, so it is saved and restored around the load.
+__device__ __forceinline__ void lds_dma16(uint32_t m0, const uint8_t* sbase, uint32_t voff) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(m0), "v"(voff), "s"(sbase)
+      : "memory");
+}
 
 __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -92,6 +120,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   int64_t s0, s1;
   shard_range(L, a.kvp, j, &s0, &s1);
   const int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
+  const int64_t last = s1 - 1;
 
   const int64_t slab = (int64_t)b * a.Hkv + kvh;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + slab * a.S_max * kRowBytes;
@@ -116,50 +145,62 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   // counts the loop waits on explicitly.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  f32x4_t acc[2][32];
-  float m2[2], lsum[2];
-  const int64_t last = s1 - 1;
-
-  // LDS byte address of the dynamic buffer ring.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)smem;
+  // Rotary-dim loads: lane i < 36 fills slot i of a 4-row group, i.e. row
+  // i / 9, chunk i % 9 of the row's last 8 chunks (the pad slot 8 repeats
+  // chunk 7).
+  const int tl_row = lane / 9;
+  const int tl_chunk = (lane % 9) == 8 ? 7 : lane % 9;
+  const uint32_t tl_off = (uint32_t)(kMainRowBytes + tl_chunk * 16);
 
-  // Issue the direct-to-LDS loads of tile `tile` into buffer `buf` (with the
-  // non-temporal hint: every cached byte is read once).  They are
-  // written as inline asm so that the compiler does not treat every later LDS
-  // read as possibly aliasing them (it would wait for all of them, including
-  // the prefetch of the next tiles); the waits are explicit below.
+  // Issue the direct-to-LDS loads of tile `tile` into buffer `buf`: this
+  // wave's kRowsPerWave rows.  Rows past the shard end (last tile only) are
+  // clamped to its last row.
   auto issue = [&](int tile, int buf) {
     const int64_t base = s0 + (int64_t)tile * kTile;
+    const uint32_t bufaddr = lds0 + (uint32_t)(buf * kBufBytes);
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      // the thread index goes through an opaque move so the ten per-lane
-      // source offsets are recomputed per tile instead of being held live
-      int tid;
-      asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
-      const int s = k * kThreads + tid;           // slot filled by this lane
-      int t = s / kStride;
-      int c = s - t * kStride;
-      if (s >= kUsed) t = 0;                      // spare slot: any in-shard chunk
-      if (c >= kChunks || s >= kUsed) c = 0;      // pad slot: likewise
-      int64_t row = base + t;
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int r = kRowsPerWave * wave + k;
+      int64_t row = base + r;
       row = row < last ? row : last;
-      const uint8_t* src = kbase + row * kRowBytes + c * 16;
-      // M0 = LDS byte address of this wave's 64 consecutive slots
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          lds0 + (uint32_t)(buf * (kSlots * 16) + (k * kThreads + wave * 64) * 16));
-      // (M0 is saved and restored around the load: the compiler owns it)
-      uint32_t m0_saved;
-      asm volatile(
-          "s_mov_b32 %0, m0\n\t"
-          "s_mov_b32 m0, %1\n\t"
-          "s_nop 0\n\t"
-          "global_load_lds_dwordx4 %2, off nt\n\t"
-          "s_mov_b32 m0, %0"
-          : "=&s"(m0_saved)
-          : "s"(dst), "v"(src)
-          : "memory");
+      lds_dma16(__builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(r * kMainStride * 16)),
+                kbase + row * kRowBytes, (uint32_t)(lane * 16));
+    }
+#pragma unroll
+    for (int h = 0; h < kRowsPerWave / 4; ++h) {
+      const int r0 = kRowsPerWave * wave + 4 * h;
+      const uint32_t m0 =
+          __builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(kMainBytes + r0 * kTailStride * 16));
+      const int64_t row0 = base + r0;
+      if (row0 + 3 <= last) {
+        if (lane < 36) lds_dma16(m0, kbase + row0 * kRowBytes, (uint32_t)(tl_row * kRowBytes) + tl_off);
+      } else {
+        // rows clamped per lane, relative to a clamped (in-shard) group base
+        const int64_t rb = row0 < last ? row0 : last;
+        int64_t row = row0 + tl_row;
+        row = row < last ? row : last;
+        const uint32_t off = (uint32_t)((row - rb) * kRowBytes) + tl_off;
+        if (lane < 36) lds_dma16(m0, kbase + rb * kRowBytes, off);
+      }
     }
   };
+
+  // Per-lane LDS read offsets within a buffer.
+  const int pk = perm16(r16);                  // token of this lane's K operand row
+  const uint32_t k_main = (uint32_t)((pk * kMainStride + g) * 16);
+  const uint32_t k_tail = (uint32_t)(kMainBytes + (pk * kTailStride + g) * 16);
+  const int rr = r16 >> 2;                     // row of the lane's 4x16 transpose group
+  const int q = r16 & 3;                       // 4-column piece of the 16 columns
+  const uint32_t v_off =
+      (uint32_t)((perm16(4 * g + rr) * kMainStride + (q >> 1)) * 16 + (q & 1) * 8);
+  // token (within the tile) of each of the lane's 8 logits, for masking
+  int tok[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) tok[e] = 16 * (e >> 2) + perm16(4 * g + (e & 3));
+
+  f32x4_t acc[2][32];
+  float m2[2], lsum[2];
 
   // Pass structure.  The accumulating pass fixes each head's reference max
   // at its first tile and never rescales the accumulator; weights may grow to
@@ -194,25 +235,31 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
       }
       __builtin_amdgcn_s_barrier();
       if (tile + 2 < ntiles) issue(tile + 2, (tile + 2) % kBufs);
-      const uint8_t* tb = smem + buf * (kSlots * 16);
-      const int64_t base = s0 + (int64_t)tile * kTile;
+      const uint8_t* tb = smem + buf * kBufBytes;
+      const int nvalid = (int)(s1 - (s0 + (int64_t)tile * kTile));   // > kTile except at the end
 
-      // ---- logits for both 16-token halves and both head blocks, with the K
-      // operands of chunk c+1 read while chunk c's MFMAs run
+      // ---- logits for both 16-token halves and both head blocks; K operands
+      // are read two chunks ahead of the MFMAs that use them
       f32x4_t s[2][2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) s[u][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* kl = tb + (r16 * kStride + g) * 16;      // this lane's K base
-      uint4 kn0 = *reinterpret_cast<const uint4*>(kl);
-      uint4 kn1 = *reinterpret_cast<const uint4*>(kl + 16 * kStride * 16);
+      auto kread = [&](int c, int u) {
+        const uint8_t* p = c < 16 ? tb + k_main + (16 * u * kMainStride + 4 * c) * 16
+                                  : tb + k_tail + (16 * u * kTailStride + 4 * (c - 16)) * 16;
+        return *reinterpret_cast<const uint4*>(p);
+      };
+      uint4 ka0 = kread(0, 0), ka1 = kread(0, 1);
+      uint4 kb0 = kread(1, 0), kb1 = kread(1, 1);
 #pragma unroll
       for (int c = 0; c < 18; ++c) {
-        const uint4 k0 = kn0, k1 = kn1;
-        if (c + 1 < 18) {
-          kn0 = *reinterpret_cast<const uint4*>(kl + 4 * (c + 1) * 16);
-          kn1 = *reinterpret_cast<const uint4*>(kl + (16 * kStride + 4 * (c + 1)) * 16);
+        const uint4 k0 = ka0, k1 = ka1;
+        ka0 = kb0;
+        ka1 = kb1;
+        if (c + 2 < 18) {
+          kb0 = kread(c + 2, 0);
+          kb1 = kread(c + 2, 1);
         }
         const bf16x8_t a0 = as_bf16x8(k0.x, k0.y, k0.z, k0.w);
         const bf16x8_t a1 = as_bf16x8(k1.x, k1.y, k1.z, k1.w);
@@ -223,7 +270,8 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- softmax weights per head (lane (n, g): tokens 16u + 4g + i)
+      // ---- softmax weights per head; lane (n, g) holds the logits of head n
+      // for tokens tok[0..7]
       bf16x8_t pop[2], pol[2];
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
@@ -231,16 +279,15 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t t = base + 16 * u + 4 * g + i;
-            x[4 * u + i] = (t < s1) ? s[u][hb][i] : -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i) x[4 * u + i] = s[u][hb][i];
+        if (nvalid < kTile) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = tok[e] < nvalid ? x[e] : -INFINITY;
+        }
         float tmax = x[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float tmax2 = tmax * c2;
+        const float tmax2 = rows4_max(tmax) * c2;
         if (max_only) {
           m2[hb] = fmaxf(m2[hb], tmax2);
           continue;
@@ -250,36 +297,39 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = fast_exp2(fmaf(x[e], c2, -m2[hb]));
-          p[e] = (x[e] == -INFINITY) ? 0.0f : pe;
+          p[e] = fast_exp2(fmaf(x[e], c2, -m2[hb]));  // masked logits give exp2(-inf) = 0
           lsum[hb] += p[e];
         }
         uint32_t ph[4], pl[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const uint32_t b0 = __float_as_uint(p[2 * rr]), b1 = __float_as_uint(p[2 * rr + 1]);
-          ph[rr] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-          pl[rr] = pack_bf16(p[2 * rr] - __uint_as_float(b0 & 0xFFFF0000u),
-                             p[2 * rr + 1] - __uint_as_float(b1 & 0xFFFF0000u));
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t b0 = __float_as_uint(p[2 * i]), b1 = __float_as_uint(p[2 * i + 1]);
+          ph[i] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+          pl[i] = pack_bf16(p[2 * i] - __uint_as_float(b0 & 0xFFFF0000u),
+                            p[2 * i + 1] - __uint_as_float(b1 & 0xFFFF0000u));
         }
         pop[hb] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         pol[hb] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
       }
       if (max_only) continue;
 
-      // ---- O^T += V^T P^T over 32 blocks of 16 value columns, one block ahead
-      const int rr = r16 >> 2;      // row of the 4x16 transpose group
-      const int q = r16 & 3;        // 4-column piece within the 16 columns
-      const uint8_t* vl0 = tb + ((4 * g + rr) * kStride + (q >> 1)) * 16 + (q & 1) * 8;
-      const uint8_t* vl1 = vl0 + 16 * kStride * 16;
-      s16x4_t vn0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vl0);
-      s16x4_t vn1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vl1);
+      // ---- O^T += V^T P^T over 32 blocks of 16 value columns; V^T operands
+      // are read two blocks ahead of their MFMAs
+      const uint8_t* vl0 = tb + v_off;                        // tokens of half 0
+      const uint8_t* vl1 = vl0 + 16 * kMainStride * 16;       // tokens of half 1
+      auto vread = [&](const uint8_t* p, int blk) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 2 * blk * 16));
+      };
+      s16x4_t va0 = vread(vl0, 0), va1 = vread(vl1, 0);
+      s16x4_t vb0 = vread(vl0, 1), vb1 = vread(vl1, 1);
 #pragma unroll
       for (int blk = 0; blk < 32; ++blk) {
-        const s16x4_t v0 = vn0, v1 = vn1;
-        if (blk + 1 < 32) {
-          vn0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vl0 + 2 * (blk + 1) * 16));
-          vn1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vl1 + 2 * (blk + 1) * 16));
+        const s16x4_t v0 = va0, v1 = va1;
+        va0 = vb0;
+        va1 = vb1;
+        if (blk + 2 < 32) {
+          vb0 = vread(vl0, blk + 2);
+          vb1 = vread(vl1, blk + 2);
         }
         const uint2 w0 = __builtin_bit_cast(uint2, v0);
         const uint2 w1 = __builtin_bit_cast(uint2, v1);
@@ -305,9 +355,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   // ---- write the normalized partial of this wave's 32 heads
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    float lt = lsum[hb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = rows4_sum(lsum[hb]);
     const bool empty = (m2[hb] == -INFINITY);
     const float inv = empty ? 0.0f : 1.0f / lt;
     const int h = head0 + 16 * hb + r16;
@@ -322,7 +370,11 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   }
 }
 
-constexpr size_t kSmemBytes = (size_t)kBufs * kSlots * 16;
+constexpr size_t kSmemBytes = (size_t)kBufs * kBufBytes;
+static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
+static_assert((kTile - 1) * kMainStride * 16 + kMainRowBytes <= kMainBytes, "row loads stay in the main region");
+static_assert(kMainBytes + (kTile - 4) * kTailStride * 16 + 4 * kTailStride * 16 <= kBufBytes,
+              "rotary loads stay in the buffer");
 
 }  // namespace
 
