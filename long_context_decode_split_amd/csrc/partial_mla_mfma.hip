@@ -20,7 +20,7 @@
 // rate at the HBM roof.
 //
 // Tiles travel HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a
-// ring of kBufs buffers, two tiles ahead.  A buffer has two regions: the first
+// ring of kBufs buffers, kAhead = 3 tiles ahead.  A buffer has two regions: the first
 // 1024 bytes of each of the 32 rows (dims 0..511) at a stride of 65 16-byte
 // slots, one row per load instruction, and the last 128 bytes (dims 512..575)
 // at a stride of 9 slots, four rows per load instruction.  Every source
@@ -62,7 +62,8 @@ constexpr int kTailStride = 9;              // 16-byte slots per row, dims 512..
 constexpr int kMainBytes = kTile * kMainStride * 16;   // 33280
 constexpr int kTailBytes = kTile * kTailStride * 16;   // 4608
 constexpr int kBufBytes = kMainBytes + kTailBytes;     // 37888
-constexpr int kBufs = 3;
+constexpr int kBufs = 4;
+constexpr int kAhead = kBufs - 1;           // tiles in flight ahead of the one computed
 constexpr int kLoads = kRowsPerWave + kRowsPerWave / 4;  // load instructions per wave per tile
 constexpr float kHeadroom = 64.0f;  // max log2 growth of P over the reference
 
@@ -76,6 +77,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
   bf16x2_t h = __builtin_convertvector(f, bf16x2_t);
   return __builtin_bit_cast(uint32_t, h);
 }
+
+// s_waitcnt immediate that waits until at most n vector memory operations
+// remain in flight (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4 and
+// lgkmcnt 11:8 left at their maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+static_assert(2 * kLoads < 64, "vmcnt range");
 
 // Token (within a 16-token half-tile) held by MFMA row m = 4a + i:
 // a = 0 -> 0,2,4,6; a = 1 -> 1,3,5,7; a = 2 -> 8,..,14; a = 3 -> 9,..,15.
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   // Q is in registers before any cache load is issued, so the only vector
   // memory operations in flight inside the tile loop are the tile loads whose
   // counts the loop waits on explicitly.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)smem;
   // Rotary-dim loads: lane i < 36 fills slot i of a 4-row group, i.e. row
@@ -220,21 +227,26 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
       }
     }
     int overflow = 0;
-    if (ntiles > 0) {
-      issue(0, 0);
-      if (ntiles > 1) issue(1, 1);
-    }
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t)
+      if (t < ntiles) issue(t, t);
     for (int tile = 0; tile < ntiles; ++tile) {
       const int buf = tile % kBufs;
-      // this tile's loads are done once at most the next tile's remain
-      // (s_waitcnt simm16 on gfx9: vmcnt in bits 3:0, expcnt 6:4, lgkmcnt 11:8)
-      if (tile + 1 < ntiles) {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);   // vmcnt(kLoads)
+      // this tile's loads are done once at most those of the tiles after it
+      // remain in flight (s_waitcnt simm16 on gfx9: vmcnt in bits 3:0 and
+      // 15:14, expcnt 6:4, lgkmcnt 11:8)
+      const int after = ntiles - 1 - tile;
+      if (after >= 2) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoads));
+      } else if (after == 1) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
       } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       }
       __builtin_amdgcn_s_barrier();
-      if (tile + 2 < ntiles) issue(tile + 2, (tile + 2) % kBufs);
+      // the buffer of tile + kAhead was last read in tile - 1, which every
+      // wave has finished at the barrier above
+      if (tile + kAhead < ntiles) issue(tile + kAhead, (tile + kAhead) % kBufs);
       const uint8_t* tb = smem + buf * kBufBytes;
       const int nvalid = (int)(s1 - (s0 + (int64_t)tile * kTile));   // > kTile except at the end
 
