@@ -33,22 +33,38 @@ METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S
 
 # HBM bytes per launch of the partial kernel measured with rocprofv3 counters
 # (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a plain 1 GiB
-# copy), keyed by (workload, kvp, sha256 prefix of the kernel source the
-# counters were taken on).  A changed kernel source no longer matches, and the
+# copy), keyed by (workload, kvp, sha256 prefix of the kernel code the
+# counters were taken on).  Changed kernel code no longer matches, and the
 # bench then reports traffic as null.  Summaries are under profiles/.
 TRAFFIC = {
-    ("helix_fp8", 32, "71b1b280f079ac15"): 17207578650,
+    ("helix_fp8", 32, "b385f0b82e79652f"): 17529276368,
+    ("helix_mxfp4", 32, "b385f0b82e79652f"): 9182880567,
+    ("gqa_bf16_varlen", 16, "b385f0b82e79652f"): 3475220072,
+    ("mla_bf16", 32, "5a82cc7521779442"): 4900503907,
 }
 KERNEL_SOURCES = {"bf16": "partial_gqa_mfma.hip", "fp8": "partial_gqa_mfma.hip",
                   "mxfp4": "partial_gqa_mfma.hip", "f32": "partial_valu.hip"}
 
 
 def kernel_hash(kv_dtype, mla=False):
+    """sha256 prefix of the partial kernel's code (its source file plus the
+    shared device header), with // comments and blank space removed, so that
+    comment edits keep the recorded counters."""
     import hashlib
+    import re
     name = "partial_mla_mfma.hip" if mla else KERNEL_SOURCES[kv_dtype]
-    path = os.path.join(HERE, "long_context_decode_split_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in (name, "kvd_device.hpp"):
+        with open(os.path.join(HERE, "long_context_decode_split_amd", "csrc", f)) as fh:
+            code = re.sub(r"//[^\n]*", "", fh.read())
+        h.update(" ".join(code.split()).encode())
+    return h.hexdigest()[:16]
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
 def log(msg):
@@ -111,6 +127,9 @@ def main():
     ap.add_argument("--kvp", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps that each start with the last-level cache flushed "
+                         "(for workloads whose cache fits in it); reported under 'cold'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (the "
                          "reference kernel for scaling HBM byte counters), and exit")
@@ -184,6 +203,7 @@ def main():
     partial_ms = [e[0].elapsed_time(e[1]) for e in evs]
     merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
     partial_avg = sum(partial_ms) / len(partial_ms)
+    step_ms = [a_ + b_ for a_, b_ in zip(partial_ms, merge_ms)]
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
 
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -212,13 +232,50 @@ def main():
                    "S": w.S_max, "kvp": kvp, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
                    "kv_bytes": kv_bytes, "flops": flops},
         "partial_us": round(partial_avg * 1e3, 2),
+        "partial_us_median": round(median(partial_ms) * 1e3, 2),
+        "partial_us_min": round(min(partial_ms) * 1e3, 2),
         "merge_us": round(sum(merge_ms) / len(merge_ms) * 1e3, 2),
+        "step_us_median": round(median(step_ms) * 1e3, 2),
+        "step_us_min": round(min(step_ms) * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": peak, "unit": "GB/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "kvd partial pass", "kernel_source_hash": khash,
                      "bytes_per_launch": kv_bytes,
                      "tflops": round(flops / (partial_avg * 1e-3) / 1e12, 2)},
     }
+    if args.cold:
+        # Each step starts after a 1 GiB write that evicts the cache from the
+        # 256 MB last-level cache; only the step itself is inside the events.
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cold_p, cold_s = [], []
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                flush.fill_(float(i))
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                step(*e)
+                torch.cuda.synchronize()
+                cold_p.append(e[0].elapsed_time(e[1]))
+                cold_s.append(e[0].elapsed_time(e[2]))
+        del flush
+        res["cold"] = {"partial_us_median": round(median(cold_p) * 1e3, 2),
+                       "step_us_median": round(median(cold_s) * 1e3, 2),
+                       "step_us_min": round(min(cold_s) * 1e3, 2),
+                       "value": round(kv_bytes / (median(cold_s) * 1e-3) / 1e9, 2), "unit": "GB/s",
+                       "note": "each step after a 1 GiB flush write; 'value' and us_per_step above "
+                               "are warm (back-to-back steps)"}
+    if w.v_aliases_k:
+        # latent heads run on bf16 MFMA: report the matrix-core share of the
+        # partial pass.  The product P.V runs twice (P as a bf16 hi + lo pair),
+        # so the executed MFMA flops exceed the algorithmic ones.
+        executed = roofline.attention_flops(w.Hq, seq, w.Dqk, 2 * w.Dv)
+        t = partial_avg * 1e-3
+        res["roofline"]["mfma"] = {
+            "peak_tflops": roofline.MFMA_BF16_FLOPS / 1e12,
+            "algorithmic_tflops": round(flops / t / 1e12, 2),
+            "algorithmic_frac": round(flops / t / roofline.MFMA_BF16_FLOPS, 4),
+            "executed_tflops": round(executed / t / 1e12, 2),
+            "executed_frac": round(executed / t / roofline.MFMA_BF16_FLOPS, 4),
+            "executed_flops": executed}
     del dev
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -195,6 +195,15 @@ WORKLOADS = {
     "mxfp4_b32_s256k": Workload("mxfp4_b32_s256k", B=32, Hq=128, Hkv=8, Dqk=128, Dv=128,
                                 S_max=1 << 18, kvp=(8, 32, 128), q_dtype="bf16",
                                 kv_dtype="mxfp4", seed=1004),
+    # One GPU's share of the Helix shape at TPA=8, KVP=8 (one KV head of 16 query
+    # heads, S/8 = 131072 resident tokens per request), split further over the
+    # GPU's own compute units; the whole cache fits the 256 MB last-level cache.
+    "helix_shard_fp8": Workload("helix_shard_fp8", B=8, Hq=16, Hkv=1, Dqk=128, Dv=128,
+                                S_max=1 << 17, kvp=(64, 16, 128), q_dtype="bf16", kv_dtype="fp8",
+                                seed=1006),
+    "helix_shard_mxfp4": Workload("helix_shard_mxfp4", B=8, Hq=16, Hkv=1, Dqk=128, Dv=128,
+                                  S_max=1 << 17, kvp=(64, 16, 128), q_dtype="bf16",
+                                  kv_dtype="mxfp4", seed=1007),
     # MLA-style: 128 query heads on one 576-wide latent head; V = first 512 dims of K.
     "mla_bf16": Workload("mla_bf16", B=8, Hq=128, Hkv=1, Dqk=576, Dv=512, S_max=1 << 19,
                          kvp=(32,), q_dtype="bf16", kv_dtype="bf16", seed=1005,

@@ -15,9 +15,8 @@
 // Work split: one workgroup of 4 waves per (shard j, request b, KV head).  The
 // shard is walked in 32-token tiles shared by all four waves; wave w owns heads
 // 32w .. 32w+31, keeping their Q (144 VGPRs) and their O^T accumulator (32 heads
-// x 512 dv, 256 AGPRs) in registers for the whole shard, so LDS traffic per
-// cached token is 4 x (1152 + 1024) bytes, within the ~128 B/clk/CU LDS read
-// rate at the HBM roof.
+// x 512 dv, 256 AGPRs) in registers for the whole shard; LDS traffic per
+// cached token is 4 x (1152 + 1024) bytes.
 //
 // Tiles travel HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a
 // ring of kBufs buffers, kAhead = 3 tiles ahead.  A buffer has two regions: the first
@@ -27,14 +26,16 @@
 // address is a wave-uniform row pointer plus a fixed lane offset.
 //
 // Within each 16-token half-tile, MFMA row m holds token perm16(m), which
-// interleaves even and odd tokens so that the LDS reads are free of bank
-// conflicts: the 8 rows read together by a ds_read_b128 of K fall on 8
-// different 16-byte bank groups (strides 65 and 9 are 1 mod 8), and the four
-// rows read by each 16-lane ds_read_b64_tr_b16 group of V are two apart, 8
-// banks from each other.  K operands are ds_read_b128 of 8 contiguous dims of
-// one token; V^T operands come from ds_read_b64_tr_b16, whose 16-lane
-// transpose turns four 16-column row segments into one column of 4 tokens per
-// lane, which is exactly the V^T MFMA operand.
+// interleaves even and odd tokens so that, in a model of 32 four-byte LDS
+// banks, the 8 rows read together by a ds_read_b128 of K fall on 8 different
+// 16-byte bank groups (strides 65 and 9 are 1 mod 8) and the four rows read
+// by each 16-lane ds_read_b64_tr_b16 group of V are 8 banks apart.  (Measured
+// on gfx950, these strided reads still cost about 8 clocks per b128 and per
+// tr16 instruction, against about 6 for a lane-contiguous b128.)  K operands
+// are ds_read_b128 of 8 contiguous dims of one token; V^T operands come from
+// ds_read_b64_tr_b16, whose 16-lane transpose turns four 16-column row
+// segments into one column of 4 tokens per lane, which is exactly the V^T
+// MFMA operand.
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
 

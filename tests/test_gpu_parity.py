@@ -212,6 +212,13 @@ def test_full_mxfp4_batch_sweep(name):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("name", ["helix_shard_fp8", "helix_shard_mxfp4"])
+def test_full_helix_shard(name):
+    """One GPU's share of the Helix shape (Hkv=1, 16 heads, S/8 tokens), split 64 ways."""
+    _check_sampled(name, 64, n_pairs=2)
+
+
+@pytest.mark.slow
 def test_full_mla_bf16():
     from long_context_decode_split_amd import kvd
     w = kvgen.WORKLOADS["mla_bf16"]
