@@ -106,10 +106,11 @@ struct Raw {
   uint32_t k[2][Layout<KV>::kKLoads * 4];      // two half-tiles
   uint32_t v[8][Layout<KV>::kVBytes / 4];      // 8 tokens
   uint32_t ks[2];                              // MXFP4: K block exponent per half-tile
-  uint32_t vs[8];                              // MXFP4: V block exponent per token
+  uint32_t vs[8];                              // MXFP4: the 4 V block exponents of each token
 };
 
-template <int KV>
+// VS16 (MXFP4 only): every slab's V scale array is 16-byte aligned.
+template <int KV, bool VS16 = false>
 __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   using Lay = Layout<KV>;
   constexpr int64_t ROW = Lay::kRowBytes;
@@ -177,7 +178,11 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   const uint32_t koff = (uint32_t)(r16 * ROW + 16 * g);
   const uint32_t voff = (uint32_t)(4 * g * ROW + Lay::kVBytes * r16);
   const uint32_t ksoff = (uint32_t)(r16 * (kD / 32) + g);
-  const uint32_t vsoff = (uint32_t)(4 * g * (kD / 32) + r16 / 4);
+  // MXFP4 V scales: the 4 exponent bytes of tokens 4g .. 4g+3 (and 16 + ...)
+  // are 16 contiguous bytes, one load each when every slab's scale array is
+  // 16-byte aligned (VS16: S_max % 4 == 0); the lane picks byte r16 / 4.
+  const uint32_t vsoff = (uint32_t)(4 * g * (kD / 32));
+  const uint32_t vs_shift = (uint32_t)(8 * (r16 / 4));
 
   // FULL: every row of the tile is inside the shard (no clamping needed).
   auto load = [&](Raw<KV>& rw, int tile, auto full_tag) {
@@ -213,19 +218,37 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
         }
       }
     }
+    if constexpr (KV == kMXFP4) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if constexpr (FULL && VS16) {
+          const u32x4_t v = stream_load16(vsbase + (base + 16 * u) * (kD / 32) + vsoff);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rw.vs[4 * u + i] = v[i];
+        } else if constexpr (FULL) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            rw.vs[4 * u + i] = stream_load4(vsbase + (base + 16 * u) * (kD / 32) + vsoff + 4 * i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            int64_t t = base + 16 * u + 4 * g + i;
+            t = t < last ? t : last;
+            rw.vs[4 * u + i] = stream_load4(vsbase + t * (kD / 32));
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int erow = 16 * (e / 4) + (e % 4);   // row of token e relative to 4g
       const uint8_t* p;
-      const uint8_t* ps = nullptr;
       if constexpr (FULL) {
         p = vt + voff + erow * ROW;
-        if constexpr (KV == kMXFP4) ps = vsbase + base * (kD / 32) + vsoff + erow * (kD / 32);
       } else {
         int64_t t = base + erow + 4 * g;
         t = t < last ? t : last;
         p = vbase + t * ROW + Lay::kVBytes * r16;
-        if constexpr (KV == kMXFP4) ps = vsbase + t * (kD / 32) + r16 / 4;
       }
       if constexpr (Lay::kVBytes == 16) {
         const u32x4_t v = stream_load16(p);
@@ -240,7 +263,6 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       } else {
         rw.v[e][0] = stream_load4(p);
       }
-      if constexpr (KV == kMXFP4) rw.vs[e] = stream_load1(ps);
     }
   };
 
@@ -333,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) cv[e][q] = rw.v[e][q];
         } else {
-          const float vsc = e8m0_to_f32_fast(rw.vs[e]);
+          const float vsc = e8m0_to_f32_fast(__builtin_amdgcn_ubfe(rw.vs[e], vs_shift, 8));
           const uint32_t w = rw.v[e][0];
           cv[e][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 0));
           cv[e][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 1));
@@ -490,7 +512,10 @@ hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(gqa_mfma_kernel<kFP8>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
       break;
     case kMXFP4:
-      hipLaunchKernelGGL(gqa_mfma_kernel<kMXFP4>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      if (a.S_max % 4 == 0)
+        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -56,6 +56,14 @@ def test_group16_long_ragged(kv):
         gc.check_full(w, kvp)
 
 
+def test_mxfp4_scale_rows_not_16b_aligned():
+    """S_max % 4 != 0 leaves each slab's E8M0 scale array off 16-byte alignment,
+    which selects the kernel variant that loads V scales 4 bytes at a time."""
+    w = W("mxfp4_smax1001", B=2, Hq=32, Hkv=2, S_max=1001, seq_lens=(1001, 37), kv_dtype="mxfp4", seed=13)
+    for kvp in (1, 3, 16):
+        gc.check_full(w, kvp)
+
+
 def test_lengths_at_tile_edges():
     for L in (1, 15, 16, 17, 31, 32, 33, 63, 64, 65):
         w = W("edge_%d" % L, B=1, Hq=16, Hkv=1, S_max=80, seq_lens=(L,), kv_dtype="bf16", seed=L)
