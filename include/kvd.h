@@ -56,9 +56,29 @@
  *    latent heads, the vector-ALU kernel otherwise).  Setting the environment
  *    variable KVD_PATH=valu before the first call restricts it to the
  *    vector-ALU kernel, e.g. to cross-check the two.
- *  - Device-side preconditions: 0 <= seq_lens[b] <= S_max.  Kernels clamp
- *    each length into [0, S_max], so no read ever leaves the cache.  A
- *    request with L = 0 yields o = 0 and lse = -inf.
+ *  - Device-side preconditions: 0 <= seq_lens[b] <= S_max (contiguous
+ *    layout) or <= kvp * S_max (sharded layouts).  Kernels clamp each length,
+ *    and each shard's length into [0, S_max], so no read ever leaves the
+ *    cache.  A request with L = 0 yields o = 0 and lse = -inf.
+ *
+ * Cache layouts (kvd_problem.layout).  Which shard stores global token
+ * position i of a request:
+ *  - KVD_LAYOUT_CONTIGUOUS: one cache [B,Hkv,S_max,D]; token i is row i, and
+ *    shards are cut at decode time by the split rule above.
+ *  - KVD_LAYOUT_STRIPED: token i belongs to shard i mod kvp, at local row
+ *    i div kvp (the inference-parallelism survey, sequence layouts section,
+ *    "Striped": rank = position mod CP, each rank storing its tokens
+ *    compactly).
+ *  - KVD_LAYOUT_STAGGERED16: tokens are dealt to shards in runs of 16: token
+ *    i belongs to shard (i div 16) mod kvp, at local row
+ *    16 * (i div (16 kvp)) + i mod 16 (Helix article, section "Then
+ *    reconfigure the same GPUs": new tokens go to one KV-parallel rank for 16
+ *    decode steps, then to the next, round-robin).
+ * A sharded cache is k.data [kvp,B,Hkv,S_max,Dqk] (v.data likewise; MXFP4
+ * scales [kvp,B,Hkv,S_max,D/32]; fp8 scales stay [B,Hkv]): shard j of
+ * request b holds its tokens in increasing position at rows 0 .. L_j - 1,
+ * and S_max is the capacity of one shard.  Decode results do not depend on
+ * the layout; shard j's partial is attention over the tokens shard j holds.
  */
 #ifndef KVD_H_
 #define KVD_H_
@@ -70,7 +90,7 @@
 extern "C" {
 #endif
 
-#define KVD_ABI_VERSION 1
+#define KVD_ABI_VERSION 2
 
 typedef enum {
   KVD_OK = 0,
@@ -86,6 +106,12 @@ typedef enum {
   KVD_MXFP4 = 3
 } kvd_dtype;
 
+typedef enum {
+  KVD_LAYOUT_CONTIGUOUS = 0,
+  KVD_LAYOUT_STRIPED = 1,
+  KVD_LAYOUT_STAGGERED16 = 2
+} kvd_layout;
+
 /* A hipStream_t (layout-compatible; NULL is the null stream). */
 typedef struct ihipStream_t* kvd_stream_t;
 
@@ -97,13 +123,16 @@ typedef struct {
   int32_t Hkv;          /* KV heads, >= 1 */
   int32_t Dqk;          /* q/k head width */
   int32_t Dv;           /* v/o head width (== Dqk except latent attention) */
-  int64_t S_max;        /* token stride of the cache, >= 1, >= every seq_len */
+  int64_t S_max;        /* token stride of the cache (of one shard for the
+                           sharded layouts), >= 1 */
   int32_t kvp;          /* shards per request, 1 .. 4096 */
   int32_t q_dtype;      /* kvd_dtype: KVD_F32 or KVD_BF16 */
   int32_t kv_dtype;     /* kvd_dtype of K and V */
   float sm_scale;       /* logit scale, >= 0 and finite; 0 means 1/sqrt(Dqk) */
   int32_t v_aliases_k;  /* nonzero: V is k[..., :Dv] (Dv <= Dqk); v.data and
                            v.scale must be NULL */
+  int32_t layout;       /* kvd_layout of the cache; zero-initialized problems
+                           are contiguous */
 } kvd_problem;
 
 /* One cache tensor: element data and, for fp8 / MXFP4, its scales. */
@@ -137,6 +166,29 @@ size_t kvd_decode_workspace_bytes(const kvd_problem* p);
 int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
                const int32_t* seq_lens, void* workspace, float* o, float* lse,
                kvd_stream_t stream);
+
+/* Append one new token per request to the cache (the decode step's KV
+ * write).  For every request b and KV head kvh, the fp32 row k_new[b,kvh,:]
+ * (Dqk values) and v_new[b,kvh,:] (Dv values) are encoded to kv_dtype and
+ * stored at global position positions[b] under p->layout (contiguous: row
+ * positions[b]; sharded: the owner shard's local row).  Encodings:
+ *   KVD_F32: copied.  KVD_BF16: round to nearest, ties to even.
+ *   KVD_FP8_E4M3: y = x / scale[b,kvh] in fp32 (the slab's existing scale,
+ *     read, not changed), then the nearest E4M3 value, ties to even,
+ *     saturated to +-448.
+ *   KVD_MXFP4: per block of 32 elements E = clamp(floor(log2 amax) - 2 + 127,
+ *     0, 254) (127 for an all-zero block), written to the row's scale bytes;
+ *     each element x * 2^(127 - E) becomes the nearest E2M1 value, ties to
+ *     even, saturated to +-6 (OCP MX).
+ * k_new [B,Hkv,Dqk] and v_new [B,Hkv,Dv] are fp32 device arrays of finite
+ * values, 4-byte aligned; v_new must be NULL when V aliases K.  positions is
+ * an int32 [B] device array; a position that is negative, or whose row falls
+ * outside the cache (contiguous: >= S_max; sharded: local row >= S_max), is
+ * skipped on the device.  k and v are the cache tensors of kvd_decode_partial
+ * (written through their const pointers).  kvp and layout of p define the
+ * map; q_dtype and sm_scale are ignored. */
+int kvd_append_kv(const kvd_problem* p, const float* k_new, const float* v_new,
+                  const int32_t* positions, kvd_kv k, kvd_kv v, kvd_stream_t stream);
 
 /* Static description of a status code. */
 const char* kvd_status_string(int status);

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libkvd.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "lse_merge.hip", "partial_valu.hip", "partial_gqa_mfma.hip",
-           "partial_mla_mfma.hip"]
+           "partial_mla_mfma.hip", "append_kv.hip"]
 
 # Per-source extra flags.  The GQA kernel keeps its MFMA accumulators in
 # ordinary VGPRs (it has room, and the occasional vector-ALU rescale of the

@@ -68,8 +68,12 @@ int check_problem(const kvd_problem* p) {
     return fail(KVD_ERR_INVALID, "MXFP4 needs Dqk and Dv multiples of 32");
   if (p->v_aliases_k && p->Dv > p->Dqk)
     return fail(KVD_ERR_INVALID, "v_aliases_k needs Dv <= Dqk");
+  if (p->layout != KVD_LAYOUT_CONTIGUOUS && p->layout != KVD_LAYOUT_STRIPED &&
+      p->layout != KVD_LAYOUT_STAGGERED16)
+    return fail(KVD_ERR_INVALID, "unknown layout %d", p->layout);
   // every byte offset into the cache must fit in int64
-  const double cache_bytes = (double)p->B * p->Hkv * (double)p->S_max *
+  const double shards = p->layout == KVD_LAYOUT_CONTIGUOUS ? 1.0 : (double)p->kvp;
+  const double cache_bytes = shards * (double)p->B * p->Hkv * (double)p->S_max *
                              (double)(p->Dqk > p->Dv ? p->Dqk : p->Dv) * elem_bits(p->kv_dtype) / 8;
   if (cache_bytes > 9.0e18) return fail(KVD_ERR_INVALID, "cache too large to index");
   const double part_elems = (double)p->kvp * p->B * p->Hq * (double)p->Dv;
@@ -77,10 +81,11 @@ int check_problem(const kvd_problem* p) {
   return KVD_OK;
 }
 
-int check_tensors(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v, const int32_t* seq_lens) {
+int check_tensors(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v, const int32_t* seq_lens,
+                  bool need_q16 = true) {
   if (q == nullptr || k.data == nullptr || seq_lens == nullptr)
     return fail(KVD_ERR_INVALID, "q, k.data and seq_lens must be non-NULL");
-  if (!aligned(q, 16) || !aligned(k.data, 16))
+  if ((need_q16 && !aligned(q, 16)) || !aligned(k.data, 16))
     return fail(KVD_ERR_INVALID, "q and k.data must be 16-byte aligned");
   if (!aligned(seq_lens, 4)) return fail(KVD_ERR_INVALID, "seq_lens must be 4-byte aligned");
   const bool scaled = p->kv_dtype == KVD_FP8_E4M3 || p->kv_dtype == KVD_MXFP4;
@@ -123,6 +128,7 @@ kvd::PartialArgs make_args(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv
   a.v_aliases_k = p->v_aliases_k != 0;
   const double s = p->sm_scale > 0.0f ? (double)p->sm_scale : 1.0 / std::sqrt((double)p->Dqk);
   a.scale_log2 = (float)(s * 1.4426950408889634);
+  a.layout = p->layout;
   return a;
 }
 
@@ -228,6 +234,45 @@ int kvd_lse_merge(int32_t kvp, int64_t rows, int32_t Dv, const float* o_part, co
   hipError_t e = kvd::launch_lse_merge(kvp, rows, Dv, o_part, lse_part, o, lse,
                                        reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVD_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kvd_append_kv(const kvd_problem* p, const float* k_new, const float* v_new,
+                  const int32_t* positions, kvd_kv k, kvd_kv v, kvd_stream_t stream) {
+  int s = check_problem(p);
+  if (s != KVD_OK) return s;
+  if (k_new == nullptr || positions == nullptr)
+    return fail(KVD_ERR_INVALID, "k_new and positions must be non-NULL");
+  if (!aligned(k_new, 4) || !aligned(positions, 4))
+    return fail(KVD_ERR_INVALID, "k_new and positions must be 4-byte aligned");
+  if (p->v_aliases_k) {
+    if (v_new != nullptr) return fail(KVD_ERR_INVALID, "v_new must be NULL when v_aliases_k is set");
+  } else {
+    if (v_new == nullptr) return fail(KVD_ERR_INVALID, "v_new must be non-NULL");
+    if (!aligned(v_new, 4)) return fail(KVD_ERR_INVALID, "v_new must be 4-byte aligned");
+  }
+  // the cache tensors follow the decode entry points' rules (q is not used)
+  s = check_tensors(p, k_new, k, v, positions, /*need_q16=*/false);
+  if (s != KVD_OK) return s;
+  kvd::AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = p->v_aliases_k ? nullptr : v_new;
+  a.positions = positions;
+  a.k = const_cast<void*>(k.data);
+  a.k_scale = const_cast<void*>(k.scale);
+  a.v = p->v_aliases_k ? nullptr : const_cast<void*>(v.data);
+  a.v_scale = p->v_aliases_k ? nullptr : const_cast<void*>(v.scale);
+  a.B = p->B;
+  a.Hkv = p->Hkv;
+  a.Dqk = p->Dqk;
+  a.Dv = p->Dv;
+  a.kvp = p->kvp;
+  a.S_max = p->S_max;
+  a.kv_format = p->kv_dtype;
+  a.v_aliases_k = p->v_aliases_k != 0;
+  a.layout = p->layout;
+  const hipError_t e = kvd::launch_append_kv(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVD_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -192,4 +192,59 @@ __device__ __forceinline__ void shard_range(int64_t L, int kvp, int j, int64_t* 
   *s1 = b < L ? b : L;
 }
 
+// Cache layouts (kvd_layout of kvd.h).
+enum CacheLayout : int { kContiguous = 0, kStriped = 1, kStaggered16 = 2 };
+
+// What shard j of request b reads for KV head kvh: the slab (index of its
+// [S_max, row] block in the cache tensor) and its token rows [s0, s1).
+//  contiguous: cache [B,Hkv,S_max,.]; the split rule cuts [0, L).
+//  striped / staggered16: cache [kvp,B,Hkv,S_max,.]; shard j holds its L_j
+//  tokens at rows [0, L_j), L_j the number of positions i < L it owns
+//  (i mod kvp == j, resp. (i div 16) mod kvp == j).
+// Lengths are clamped so that no row outside the slab is ever read.
+struct ShardSpan {
+  int64_t slab, s0, s1;
+};
+
+__device__ __forceinline__ ShardSpan shard_span(int layout, int64_t L, int64_t S_max, int kvp,
+                                                int B, int Hkv, int j, int b, int kvh) {
+  ShardSpan sp;
+  if (layout == kContiguous) {
+    L = L < 0 ? 0 : (L > S_max ? S_max : L);
+    sp.slab = (int64_t)b * Hkv + kvh;
+    shard_range(L, kvp, j, &sp.s0, &sp.s1);
+    return sp;
+  }
+  const int64_t cap = S_max * kvp;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  int64_t Lj;
+  if (layout == kStriped) {
+    Lj = L > j ? (L - 1 - j) / kvp + 1 : 0;
+  } else {
+    const int64_t run = 16 * (int64_t)kvp;
+    const int64_t full = L / run;
+    int64_t rem = L - full * run - 16 * (int64_t)j;
+    rem = rem < 0 ? 0 : (rem > 16 ? 16 : rem);
+    Lj = 16 * full + rem;
+  }
+  sp.slab = ((int64_t)j * B + b) * Hkv + kvh;
+  sp.s0 = 0;
+  sp.s1 = Lj < S_max ? Lj : S_max;
+  return sp;
+}
+
+// Where global position i lives: shard *j, row *r (contiguous: shard 0, row i).
+__device__ __forceinline__ void token_home(int layout, int64_t i, int kvp, int* j, int64_t* r) {
+  if (layout == kStriped) {
+    *j = (int)(i % kvp);
+    *r = i / kvp;
+  } else if (layout == kStaggered16) {
+    *j = (int)((i / 16) % kvp);
+    *r = 16 * (i / (16 * (int64_t)kvp)) + i % 16;
+  } else {
+    *j = 0;
+    *r = i;
+  }
+}
+
 }  // namespace kvd

@@ -22,6 +22,23 @@ struct PartialArgs {
   int32_t kv_format;      // KvFormat
   int32_t v_aliases_k;
   float scale_log2;       // sm_scale * log2(e)
+  int32_t layout;         // CacheLayout
+};
+
+// Arguments of one append (kvd_append_kv), already validated by api.cpp.
+struct AppendArgs {
+  const float* k_new;     // [B,Hkv,Dqk]
+  const float* v_new;     // [B,Hkv,Dv]; nullptr when V aliases K
+  const int32_t* positions;
+  void* k;
+  void* k_scale;
+  void* v;
+  void* v_scale;
+  int32_t B, Hkv, Dqk, Dv, kvp;
+  int64_t S_max;
+  int32_t kv_format;
+  int32_t v_aliases_k;
+  int32_t layout;
 };
 
 // Each family reports whether it handles a problem, then launches it.
@@ -33,6 +50,8 @@ hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream);
 
 bool mla_mfma_supports(const PartialArgs& a);
 hipError_t launch_partial_mla_mfma(const PartialArgs& a, hipStream_t stream);
+
+hipError_t launch_append_kv(const AppendArgs& a, hipStream_t stream);
 
 hipError_t launch_lse_merge(int32_t kvp, int64_t rows, int32_t Dv, const float* o_part,
                             const float* lse_part, float* o, float* lse, hipStream_t stream);

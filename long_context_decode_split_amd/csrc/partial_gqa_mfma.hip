@@ -131,21 +131,20 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   const int b = flat % a.B;
   const int j = flat / a.B;
 
-  int64_t L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.S_max ? a.S_max : L);
-  int64_t s0, s1;
-  shard_range(L, a.kvp, j, &s0, &s1);
+  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
+  const int64_t s0 = span.s0, s1 = span.s1;
+  const int64_t slab = span.slab;                  // cache block of this shard
+  const int64_t bh = (int64_t)b * a.Hkv + kvh;     // fp8 scales are per (request, KV head)
   const int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
 
-  const int64_t slab = (int64_t)b * a.Hkv + kvh;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + slab * a.S_max * ROW;
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + slab * a.S_max * ROW;
   const uint8_t* ksbase = nullptr;
   const uint8_t* vsbase = nullptr;
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (KV == kFP8) {
-    kscale = static_cast<const float*>(a.k_scale)[slab];
-    vscale = static_cast<const float*>(a.v_scale)[slab];
+    kscale = static_cast<const float*>(a.k_scale)[bh];
+    vscale = static_cast<const float*>(a.v_scale)[bh];
   }
   if constexpr (KV == kMXFP4) {
     ksbase = static_cast<const uint8_t*>(a.k_scale) + slab * a.S_max * (kD / 32);

@@ -123,14 +123,12 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   const int b = flat % a.B;
   const int j = flat / a.B;
 
-  int64_t L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.S_max ? a.S_max : L);
-  int64_t s0, s1;
-  shard_range(L, a.kvp, j, &s0, &s1);
+  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
+  const int64_t s0 = span.s0, s1 = span.s1;
+  const int64_t slab = span.slab;                  // cache block of this shard
   const int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
   const int64_t last = s1 - 1;
 
-  const int64_t slab = (int64_t)b * a.Hkv + kvh;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + slab * a.S_max * kRowBytes;
   const float c2 = a.scale_log2;
   const int head0 = kvh * kHeads + wave * 32;

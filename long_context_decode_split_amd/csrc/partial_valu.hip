@@ -57,12 +57,11 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
   const int li = lane & 15;
   const int row = wave * 4 + (lane >> 4);
 
-  int64_t L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.S_max ? a.S_max : L);
-  int64_t s0, s1;
-  shard_range(L, a.kvp, j, &s0, &s1);
+  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
+  const int64_t s0 = span.s0, s1 = span.s1;
+  const int64_t slab = span.slab;                  // cache block of this shard
+  const int64_t bh = (int64_t)b * a.Hkv + kvh;     // fp8 scales are per (request, KV head)
 
-  const int64_t slab = (int64_t)b * a.Hkv + kvh;
   const uint8_t* kp = static_cast<const uint8_t*>(a.k) + slab * a.S_max * KROW + li * KLANE;
   const uint8_t* vp = ALIAS ? static_cast<const uint8_t*>(a.k) + slab * a.S_max * KROW + li * VLANE
                             : static_cast<const uint8_t*>(a.v) + slab * a.S_max * VROW + li * VLANE;
@@ -70,8 +69,8 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
   const uint8_t* vsp = nullptr;
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (KV == kFP8) {
-    kscale = static_cast<const float*>(a.k_scale)[slab];
-    vscale = ALIAS ? kscale : static_cast<const float*>(a.v_scale)[slab];
+    kscale = static_cast<const float*>(a.k_scale)[bh];
+    vscale = ALIAS ? kscale : static_cast<const float*>(a.v_scale)[bh];
   }
   if constexpr (KV == kMXFP4) {
     ksp = static_cast<const uint8_t*>(a.k_scale) + slab * a.S_max * (DQK / 32) + (li * EK) / 32;

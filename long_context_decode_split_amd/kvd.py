@@ -24,18 +24,21 @@ LIB_PATH = os.path.join(_HERE, "libkvd.so")
 KVD_OK, KVD_ERR_INVALID, KVD_ERR_UNSUPPORTED, KVD_ERR_HIP = 0, 1, 2, 3
 KVD_F32, KVD_BF16, KVD_FP8_E4M3, KVD_MXFP4 = 0, 1, 2, 3
 DTYPE_CODES = {"f32": KVD_F32, "bf16": KVD_BF16, "fp8": KVD_FP8_E4M3, "mxfp4": KVD_MXFP4}
+KVD_LAYOUT_CONTIGUOUS, KVD_LAYOUT_STRIPED, KVD_LAYOUT_STAGGERED16 = 0, 1, 2
+LAYOUT_CODES = {"contiguous": KVD_LAYOUT_CONTIGUOUS, "striped": KVD_LAYOUT_STRIPED,
+                "staggered16": KVD_LAYOUT_STAGGERED16}
 
 # Every symbol include/kvd.h declares.
 EXPORTED = ("kvd_decode_partial", "kvd_lse_merge", "kvd_decode_workspace_bytes", "kvd_decode",
-            "kvd_status_string", "kvd_last_error", "kvd_abi_version")
-ABI_VERSION = 1
+            "kvd_append_kv", "kvd_status_string", "kvd_last_error", "kvd_abi_version")
+ABI_VERSION = 2
 
 
 class KvdProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("S_max", ctypes.c_int64),
                 ("kvp", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("sm_scale", ctypes.c_float), ("v_aliases_k", ctypes.c_int32)]
+                ("sm_scale", ctypes.c_float), ("v_aliases_k", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class KvdKV(ctypes.Structure):
@@ -74,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.kvd_decode_workspace_bytes.restype = ctypes.c_size_t
         L.kvd_decode.argtypes = [P, vp, KvdKV, KvdKV, vp, vp, vp, vp, vp]
         L.kvd_decode.restype = ctypes.c_int
+        L.kvd_append_kv.argtypes = [P, vp, vp, vp, KvdKV, KvdKV, vp]
+        L.kvd_append_kv.restype = ctypes.c_int
         L.kvd_status_string.argtypes = [ctypes.c_int]
         L.kvd_status_string.restype = ctypes.c_char_p
         L.kvd_last_error.argtypes = []
@@ -86,11 +91,15 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def problem(B, Hq, Hkv, Dqk, Dv, S_max, kvp, q_dtype, kv_dtype, sm_scale=0.0, v_aliases_k=False) -> KvdProblem:
-    """A kvd_problem; dtypes may be KVD_* codes or 'f32' / 'bf16' / 'fp8' / 'mxfp4'."""
+def problem(B, Hq, Hkv, Dqk, Dv, S_max, kvp, q_dtype, kv_dtype, sm_scale=0.0, v_aliases_k=False,
+            layout="contiguous") -> KvdProblem:
+    """A kvd_problem; dtypes may be KVD_* codes or 'f32' / 'bf16' / 'fp8' / 'mxfp4', the layout a
+    KVD_LAYOUT_* code or 'contiguous' / 'striped' / 'staggered16'."""
     qd = DTYPE_CODES.get(q_dtype, q_dtype)
     kd = DTYPE_CODES.get(kv_dtype, kv_dtype)
-    return KvdProblem(B, Hq, Hkv, Dqk, Dv, S_max, kvp, qd, kd, float(sm_scale), int(bool(v_aliases_k)))
+    lay = LAYOUT_CODES.get(layout, layout)
+    return KvdProblem(B, Hq, Hkv, Dqk, Dv, S_max, kvp, qd, kd, float(sm_scale), int(bool(v_aliases_k)),
+                      int(lay))
 
 
 def _ptr(x):
@@ -146,6 +155,11 @@ def kvd_decode_workspace_bytes(p: KvdProblem) -> int:
 def kvd_decode(p: KvdProblem, q, k, v, seq_lens, workspace, o, lse, stream=None) -> None:
     _check(lib().kvd_decode(ctypes.byref(p), _ptr(q), _kv(k), _kv(v), _ptr(seq_lens), _ptr(workspace),
                             _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def kvd_append_kv(p: KvdProblem, k_new, v_new, positions, k, v, stream=None) -> None:
+    _check(lib().kvd_append_kv(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(positions), _kv(k), _kv(v),
+                               _stream(stream)))
 
 
 def kvd_status_string(status: int) -> str:

@@ -192,7 +192,8 @@ def encode_row(kv_dtype: str, x_f32: np.ndarray, fp8_scale: Optional[float] = No
 def append(p: Problem, layout: str, kvp: int, cache: dict, positions: Sequence[int],
            k_new: np.ndarray, v_new: Optional[np.ndarray]) -> None:
     """Encode token rows k_new/v_new [B,Hkv,D] (fp32) and store them at global
-    position positions[b] of each request, in place.
+    position positions[b] of each request, in place; a negative position, or
+    one whose row falls outside the cache, is skipped.
 
     cache: {"k": data, "k_scale": scales or None, "v": ..., "v_scale": ...}
     laid out per `layout` (contiguous [B,Hkv,S_max,...]; sharded
@@ -207,11 +208,17 @@ def append(p: Problem, layout: str, kvp: int, cache: dict, positions: Sequence[i
                 data, sc = cache[name], cache[name + "_scale"]
                 fscale = float(sc[b, kvh]) if p.kv_dtype == "fp8" else None
                 row, rsc = encode_row(p.kv_dtype, x[b, kvh, :D], fscale)
+                if i < 0:
+                    continue                      # positions outside the cache are skipped
                 if layout == "contiguous":
                     idx = (b, kvh, i)
+                    cap = data.shape[2]
                 else:
                     j, r = owner(i, kvp, layout)
                     idx = (j, b, kvh, r)
+                    cap = data.shape[3]
+                if idx[-1] >= cap:
+                    continue
                 data[idx] = row
                 if p.kv_dtype == "mxfp4":
                     sc[idx] = rsc

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvd.kvd_abi_version() == kvd.ABI_VERSION == 1
+    assert kvd.kvd_abi_version() == kvd.ABI_VERSION == 2
     for s in range(4):
         assert kvd.kvd_status_string(s).startswith(("KVD_OK", "KVD_ERR"))
     assert "unknown" in kvd.kvd_status_string(99)
@@ -74,6 +74,7 @@ def call_decode(p, ws=FAKE, o=FAKE, lse=FAKE, k=(FAKE, FAKE), v=(FAKE, FAKE)):
     (dict(q_dtype=7), INV), (dict(kv_dtype=9), INV), (dict(q_dtype="fp8"), INV),
     (dict(sm_scale=-1.0), INV), (dict(sm_scale=float("inf")), INV), (dict(sm_scale=float("nan")), INV),
     (dict(kv_dtype="mxfp4", Dqk=48, Dv=48), INV),
+    (dict(layout=3), INV), (dict(layout=-1), INV),
     (dict(Dqk=96, Dv=96), UNS),             # well formed, no kernel for this width
     (dict(Dqk=128, Dv=64), UNS),
 ])
@@ -148,3 +149,24 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         kvd._ptr(torch.zeros(4))
+
+
+def call_append(p, k_new=FAKE, v_new=FAKE, pos=FAKE, k=(FAKE, FAKE), v=(FAKE, FAKE)):
+    return kvd.lib().kvd_append_kv(ctypes.byref(p), k_new, v_new, pos, kvd._kv(k), kvd._kv(v), None)
+
+
+@pytest.mark.parametrize("args", [
+    dict(k_new=None), dict(k_new=FAKE + 2), dict(v_new=None), dict(v_new=FAKE + 1),
+    dict(pos=None), dict(pos=FAKE + 2), dict(k=(None, FAKE)), dict(k=(FAKE, None)),
+    dict(v=(FAKE + 4, FAKE)), dict(v=(FAKE, None)),
+])
+def test_append_rejects_bad_pointers(args):
+    for layout in ("contiguous", "striped", "staggered16"):
+        assert call_append(good_problem(layout=layout), **args) == INV
+
+
+def test_append_alias_and_problem_rules():
+    p = good_problem(kv_dtype="bf16", v_aliases_k=True, Dqk=576, Dv=512, Hkv=1, Hq=128)
+    assert call_append(p, k=(FAKE, None), v=(None, None)) == INV          # v_new must be NULL
+    assert call_append(good_problem(layout=7)) == INV
+    assert call_append(good_problem(B=0)) == INV
