@@ -125,6 +125,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="helix_fp8")
     ap.add_argument("--kvp", type=int, default=None)
+    ap.add_argument("--layout", default="contiguous", choices=["contiguous", "striped", "staggered16"],
+                    help="cache layout; a sharded layout views the generated cache as kvp shards of "
+                         "S/kvp rows (same bytes, same per-step traffic)")
+    ap.add_argument("--no-append", action="store_true", help="skip timing kvd_append_kv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold", action="store_true",
@@ -163,7 +167,24 @@ def main():
     dev = generate_on_device(w, progress=log)
     log("inputs ready in %.1f s" % (time.time() - t0))
 
-    p = kvd.problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, w.S_max, kvp, w.q_dtype, w.kv_dtype, 0.0, w.v_aliases_k)
+    S_cache = w.S_max
+    if args.layout != "contiguous":
+        # the same generated bytes viewed as kvp shards of S/kvp rows each
+        if w.S_max % kvp:
+            raise SystemExit("S_max %d is not a multiple of kvp %d" % (w.S_max, kvp))
+        S_cache = w.S_max // kvp
+        def shard_view(t, per_row_scale):
+            if t is None:
+                return None
+            if not per_row_scale:
+                return t
+            return t.view((kvp, w.B, w.Hkv, S_cache) + tuple(t.shape[3:]))
+        mx = w.kv_dtype == "mxfp4"
+        dev.k = (shard_view(dev.k[0], True), shard_view(dev.k[1], mx))
+        if dev.v is not None:
+            dev.v = (shard_view(dev.v[0], True), shard_view(dev.v[1], mx))
+    p = kvd.problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, S_cache, kvp, w.q_dtype, w.kv_dtype, 0.0, w.v_aliases_k,
+                    layout=args.layout)
     f32 = dict(dtype=torch.float32, device="cuda")
     o_part = torch.empty((kvp, w.B, w.Hq, w.Dv), **f32)
     lse_part = torch.empty((kvp, w.B, w.Hq), **f32)
@@ -228,7 +249,7 @@ def main():
         "arith": "f32 vector ALU" if w.kv_dtype == "f32" else
                  "bf16 MFMA on exactly decoded %s cache, fp32 accumulate and softmax" % w.kv_dtype,
         "data": "synthetic (seeded N(0,1), encoded to the cache format)",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Hsz": w.Dqk, "Dv": w.Dv,
+        "config": {"workload": w.name, "layout": args.layout, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Hsz": w.Dqk, "Dv": w.Dv,
                    "S": w.S_max, "kvp": kvp, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
                    "kv_bytes": kv_bytes, "flops": flops},
         "partial_us": round(partial_avg * 1e3, 2),
@@ -243,6 +264,23 @@ def main():
                      "bytes_per_launch": kv_bytes,
                      "tflops": round(flops / (partial_avg * 1e-3) / 1e12, 2)},
     }
+    if not args.no_append:
+        # one decode step's KV write: a new fp32 token row per (request, KV head),
+        # appended at the last position of every request
+        kn = torch.randn((w.B, w.Hkv, w.Dqk), dtype=torch.float32, device="cuda")
+        vn = None if w.v_aliases_k else torch.randn((w.B, w.Hkv, w.Dv), dtype=torch.float32, device="cuda")
+        pos = torch.full((w.B,), w.S_max - 1, dtype=torch.int32, device="cuda")
+        app = []
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup + args.steps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(stream)
+                kvd.kvd_append_kv(p, kn, vn, pos, dev.k, dev.v, stream)
+                e[1].record(stream)
+                torch.cuda.synchronize()
+                if i >= args.warmup:
+                    app.append(e[0].elapsed_time(e[1]))
+        res["append_us_median"] = round(median(app) * 1e3, 2)
     if args.cold:
         # Each step starts after a 1 GiB write that evicts the cache from the
         # 256 MB last-level cache; only the step itself is inside the events.
