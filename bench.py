@@ -125,9 +125,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="helix_fp8")
     ap.add_argument("--kvp", type=int, default=None)
-    ap.add_argument("--layout", default="contiguous", choices=["contiguous", "striped", "staggered16"],
+    ap.add_argument("--layout", default="contiguous", choices=["contiguous", "striped", "staggered16", "paged"],
                     help="cache layout; a sharded layout views the generated cache as kvp shards of "
-                         "S/kvp rows (same bytes, same per-step traffic)")
+                         "S/kvp rows, the paged layout as a pool of blocks handed to the requests in "
+                         "a seeded random order (same bytes, same per-step traffic)")
+    ap.add_argument("--block-len", type=int, default=16, help="tokens per block of the paged layout")
     ap.add_argument("--no-append", action="store_true", help="skip timing kvd_append_kv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -168,7 +170,25 @@ def main():
     log("inputs ready in %.1f s" % (time.time() - t0))
 
     S_cache = w.S_max
-    if args.layout != "contiguous":
+    paging = {}
+    if args.layout == "paged":
+        bl = args.block_len
+        if w.S_max % bl:
+            raise SystemExit("S_max %d is not a multiple of block_len %d" % (w.S_max, bl))
+        max_blocks = w.S_max // bl
+        num_blocks = w.B * max_blocks
+        def pool_view(t, per_row):
+            if t is None or not per_row:
+                return t
+            return t.view((num_blocks, w.Hkv, bl) + tuple(t.shape[3:]))
+        mx = w.kv_dtype == "mxfp4"
+        dev.k = (pool_view(dev.k[0], True), pool_view(dev.k[1], mx))
+        if dev.v is not None:
+            dev.v = (pool_view(dev.v[0], True), pool_view(dev.v[1], mx))
+        gen = torch.Generator().manual_seed(1234)
+        table = torch.randperm(num_blocks, generator=gen).to(torch.int32).view(w.B, max_blocks).cuda()
+        paging = dict(block_len=bl, max_blocks=max_blocks, num_blocks=num_blocks, block_table=table)
+    elif args.layout != "contiguous":
         # the same generated bytes viewed as kvp shards of S/kvp rows each
         if w.S_max % kvp:
             raise SystemExit("S_max %d is not a multiple of kvp %d" % (w.S_max, kvp))
@@ -184,7 +204,7 @@ def main():
         if dev.v is not None:
             dev.v = (shard_view(dev.v[0], True), shard_view(dev.v[1], mx))
     p = kvd.problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, S_cache, kvp, w.q_dtype, w.kv_dtype, 0.0, w.v_aliases_k,
-                    layout=args.layout)
+                    layout=args.layout, **paging)
     f32 = dict(dtype=torch.float32, device="cuda")
     o_part = torch.empty((kvp, w.B, w.Hq, w.Dv), **f32)
     lse_part = torch.empty((kvp, w.B, w.Hq), **f32)
@@ -249,7 +269,8 @@ def main():
         "arith": "f32 vector ALU" if w.kv_dtype == "f32" else
                  "bf16 MFMA on exactly decoded %s cache, fp32 accumulate and softmax" % w.kv_dtype,
         "data": "synthetic (seeded N(0,1), encoded to the cache format)",
-        "config": {"workload": w.name, "layout": args.layout, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Hsz": w.Dqk, "Dv": w.Dv,
+        "config": {"workload": w.name, "layout": args.layout,
+                   "block_len": args.block_len if args.layout == "paged" else None, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Hsz": w.Dqk, "Dv": w.Dv,
                    "S": w.S_max, "kvp": kvp, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
                    "kv_bytes": kv_bytes, "flops": flops},
         "partial_us": round(partial_avg * 1e3, 2),

@@ -74,11 +74,23 @@
  *    16 * (i div (16 kvp)) + i mod 16 (Helix article, section "Then
  *    reconfigure the same GPUs": new tokens go to one KV-parallel rank for 16
  *    decode steps, then to the next, round-robin).
+ *  - KVD_LAYOUT_PAGED: a pool of fixed-size blocks [num_blocks,Hkv,
+ *    block_len,D] shared by all requests (the per-rank block cache of the
+ *    "Attention DP" design note, section "KV Cache"); block_table
+ *    [B,max_blocks] (int32, device) lists each request's blocks in order, so
+ *    token i of request b is row i mod block_len of block
+ *    block_table[b, i div block_len].  Shards are cut by the split rule over
+ *    token positions, as for the contiguous layout.
  * A sharded cache is k.data [kvp,B,Hkv,S_max,Dqk] (v.data likewise; MXFP4
  * scales [kvp,B,Hkv,S_max,D/32]; fp8 scales stay [B,Hkv]): shard j of
  * request b holds its tokens in increasing position at rows 0 .. L_j - 1,
- * and S_max is the capacity of one shard.  Decode results do not depend on
- * the layout; shard j's partial is attention over the tokens shard j holds.
+ * and S_max is the capacity of one shard.  A paged cache is k.data
+ * [num_blocks,Hkv,block_len,Dqk] (MXFP4 scales [num_blocks,Hkv,block_len,
+ * D/32]; fp8 scales stay [B,Hkv]); block_len is a power of two in
+ * [16, 2^20], S_max is not used, lengths are clamped to max_blocks *
+ * block_len and block ids into [0, num_blocks).  Decode results do not
+ * depend on the layout; shard j's partial is attention over the tokens shard
+ * j holds.
  */
 #ifndef KVD_H_
 #define KVD_H_
@@ -90,7 +102,7 @@
 extern "C" {
 #endif
 
-#define KVD_ABI_VERSION 2
+#define KVD_ABI_VERSION 3
 
 typedef enum {
   KVD_OK = 0,
@@ -109,7 +121,8 @@ typedef enum {
 typedef enum {
   KVD_LAYOUT_CONTIGUOUS = 0,
   KVD_LAYOUT_STRIPED = 1,
-  KVD_LAYOUT_STAGGERED16 = 2
+  KVD_LAYOUT_STAGGERED16 = 2,
+  KVD_LAYOUT_PAGED = 3
 } kvd_layout;
 
 /* A hipStream_t (layout-compatible; NULL is the null stream). */
@@ -133,6 +146,10 @@ typedef struct {
                            v.scale must be NULL */
   int32_t layout;       /* kvd_layout of the cache; zero-initialized problems
                            are contiguous */
+  int32_t block_len;    /* KVD_LAYOUT_PAGED only: tokens per block */
+  int32_t max_blocks;   /* KVD_LAYOUT_PAGED only: columns of block_table */
+  int64_t num_blocks;   /* KVD_LAYOUT_PAGED only: blocks in the pool */
+  const int32_t* block_table;  /* KVD_LAYOUT_PAGED only: device [B,max_blocks] */
 } kvd_problem;
 
 /* One cache tensor: element data and, for fp8 / MXFP4, its scales. */
@@ -171,7 +188,8 @@ int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
  * write).  For every request b and KV head kvh, the fp32 row k_new[b,kvh,:]
  * (Dqk values) and v_new[b,kvh,:] (Dv values) are encoded to kv_dtype and
  * stored at global position positions[b] under p->layout (contiguous: row
- * positions[b]; sharded: the owner shard's local row).  Encodings:
+ * positions[b]; sharded: the owner shard's local row; paged: the row of the
+ * position's block in the block table).  Encodings:
  *   KVD_F32: copied.  KVD_BF16: round to nearest, ties to even.
  *   KVD_FP8_E4M3: y = x / scale[b,kvh] in fp32 (the slab's existing scale,
  *     read, not changed), then the nearest E4M3 value, ties to even,
@@ -183,8 +201,9 @@ int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
  * k_new [B,Hkv,Dqk] and v_new [B,Hkv,Dv] are fp32 device arrays of finite
  * values, 4-byte aligned; v_new must be NULL when V aliases K.  positions is
  * an int32 [B] device array; a position that is negative, or whose row falls
- * outside the cache (contiguous: >= S_max; sharded: local row >= S_max), is
- * skipped on the device.  k and v are the cache tensors of kvd_decode_partial
+ * outside the cache (contiguous: >= S_max; sharded: local row >= S_max;
+ * paged: position >= max_blocks * block_len or a block id outside
+ * [0, num_blocks)), is skipped on the device.  k and v are the cache tensors of kvd_decode_partial
  * (written through their const pointers).  kvp and layout of p define the
  * map; q_dtype and sm_scale are ignored. */
 int kvd_append_kv(const kvd_problem* p, const float* k_new, const float* v_new,

@@ -69,11 +69,24 @@ int check_problem(const kvd_problem* p) {
   if (p->v_aliases_k && p->Dv > p->Dqk)
     return fail(KVD_ERR_INVALID, "v_aliases_k needs Dv <= Dqk");
   if (p->layout != KVD_LAYOUT_CONTIGUOUS && p->layout != KVD_LAYOUT_STRIPED &&
-      p->layout != KVD_LAYOUT_STAGGERED16)
+      p->layout != KVD_LAYOUT_STAGGERED16 && p->layout != KVD_LAYOUT_PAGED)
     return fail(KVD_ERR_INVALID, "unknown layout %d", p->layout);
+  double rows;   // cache rows per KV head and request slot, for the size check
+  if (p->layout == KVD_LAYOUT_PAGED) {
+    const int bl = p->block_len;
+    if (bl < 16 || bl > (1 << 20) || (bl & (bl - 1)) != 0)
+      return fail(KVD_ERR_INVALID, "block_len must be a power of two in [16, 2^20] (got %d)", bl);
+    if (p->max_blocks < 1) return fail(KVD_ERR_INVALID, "max_blocks must be >= 1");
+    if (p->num_blocks < 1) return fail(KVD_ERR_INVALID, "num_blocks must be >= 1");
+    if (p->block_table == nullptr || !aligned(p->block_table, 4))
+      return fail(KVD_ERR_INVALID, "block_table must be non-NULL and 4-byte aligned");
+    if ((double)p->max_blocks * bl > 2.0e9) return fail(KVD_ERR_UNSUPPORTED, "max_blocks*block_len too large");
+    rows = (double)p->num_blocks * bl / p->B;
+  } else {
+    rows = (p->layout == KVD_LAYOUT_CONTIGUOUS ? 1.0 : (double)p->kvp) * (double)p->S_max;
+  }
   // every byte offset into the cache must fit in int64
-  const double shards = p->layout == KVD_LAYOUT_CONTIGUOUS ? 1.0 : (double)p->kvp;
-  const double cache_bytes = shards * (double)p->B * p->Hkv * (double)p->S_max *
+  const double cache_bytes = (double)p->B * p->Hkv * rows *
                              (double)(p->Dqk > p->Dv ? p->Dqk : p->Dv) * elem_bits(p->kv_dtype) / 8;
   if (cache_bytes > 9.0e18) return fail(KVD_ERR_INVALID, "cache too large to index");
   const double part_elems = (double)p->kvp * p->B * p->Hq * (double)p->Dv;
@@ -105,6 +118,24 @@ int check_tensors(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v, const
   return KVD_OK;
 }
 
+// Paged caches: the block table and log2(block_len); S_max becomes the
+// request capacity max_blocks * block_len, which bounds every length.
+template <class Args>
+void set_paging(const kvd_problem* p, Args* a) {
+  a->block_table = nullptr;
+  a->log2_block = 0;
+  a->max_blocks = 0;
+  a->num_blocks = 0;
+  if (p->layout != KVD_LAYOUT_PAGED) return;
+  int lg = 0;
+  while ((1 << lg) < p->block_len) ++lg;
+  a->block_table = p->block_table;
+  a->log2_block = lg;
+  a->max_blocks = p->max_blocks;
+  a->num_blocks = p->num_blocks;
+  a->S_max = (int64_t)p->max_blocks << lg;
+}
+
 kvd::PartialArgs make_args(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
                            const int32_t* seq_lens, float* o_part, float* lse_part) {
   kvd::PartialArgs a{};
@@ -123,6 +154,7 @@ kvd::PartialArgs make_args(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv
   a.Dv = p->Dv;
   a.kvp = p->kvp;
   a.S_max = p->S_max;
+  set_paging(p, &a);
   a.q_bf16 = p->q_dtype == KVD_BF16;
   a.kv_format = p->kv_dtype;
   a.v_aliases_k = p->v_aliases_k != 0;
@@ -271,6 +303,7 @@ int kvd_append_kv(const kvd_problem* p, const float* k_new, const float* v_new,
   a.kv_format = p->kv_dtype;
   a.v_aliases_k = p->v_aliases_k != 0;
   a.layout = p->layout;
+  set_paging(p, &a);
   const hipError_t e = kvd::launch_append_kv(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVD_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -72,17 +72,25 @@ __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs a) {
 
   const int64_t pos = a.positions[b];
   if (pos < 0) return;
-  int j;
-  int64_t r;
-  token_home(a.layout, pos, a.kvp, &j, &r);
-  if (r >= a.S_max) return;
   const int64_t bh = (int64_t)b * a.Hkv + kvh;
-  const int64_t slab = a.layout == kContiguous ? bh : ((int64_t)j * a.B + b) * a.Hkv + kvh;
+  int64_t row;
+  if (a.layout == kPaged) {
+    if (pos >= ((int64_t)a.max_blocks << a.log2_block)) return;
+    const int64_t pb = a.block_table[(int64_t)b * a.max_blocks + (pos >> a.log2_block)];
+    if (pb < 0 || pb >= a.num_blocks) return;
+    row = ((pb * a.Hkv + kvh) << a.log2_block) + (pos & ((1 << a.log2_block) - 1));
+  } else {
+    int j;
+    int64_t r;
+    token_home(a.layout, pos, a.kvp, &j, &r);
+    if (r >= a.S_max) return;
+    const int64_t slab = a.layout == kContiguous ? bh : ((int64_t)j * a.B + b) * a.Hkv + kvh;
+    row = slab * a.S_max + r;
+  }
   const int D = which ? a.Dv : a.Dqk;
   const float* x = (which ? a.v_new : a.k_new) + bh * D;
   uint8_t* data = static_cast<uint8_t*>(which ? a.v : a.k);
   void* scale = which ? a.v_scale : a.k_scale;
-  const int64_t row = slab * a.S_max + r;
 
   if (a.kv_format == kF32) {
     float* dst = reinterpret_cast<float*>(data) + row * D;

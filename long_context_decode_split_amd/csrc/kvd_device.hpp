@@ -193,7 +193,7 @@ __device__ __forceinline__ void shard_range(int64_t L, int kvp, int j, int64_t* 
 }
 
 // Cache layouts (kvd_layout of kvd.h).
-enum CacheLayout : int { kContiguous = 0, kStriped = 1, kStaggered16 = 2 };
+enum CacheLayout : int { kContiguous = 0, kStriped = 1, kStaggered16 = 2, kPaged = 3 };
 
 // What shard j of request b reads for KV head kvh: the slab (index of its
 // [S_max, row] block in the cache tensor) and its token rows [s0, s1).
@@ -209,7 +209,9 @@ struct ShardSpan {
 __device__ __forceinline__ ShardSpan shard_span(int layout, int64_t L, int64_t S_max, int kvp,
                                                 int B, int Hkv, int j, int b, int kvh) {
   ShardSpan sp;
-  if (layout == kContiguous) {
+  if (layout == kContiguous || layout == kPaged) {
+    // (paged: S_max is the request capacity max_blocks * block_len; rows are
+    // found through the block table, see phys_row)
     L = L < 0 ? 0 : (L > S_max ? S_max : L);
     sp.slab = (int64_t)b * Hkv + kvh;
     shard_range(L, kvp, j, &sp.s0, &sp.s1);
@@ -231,6 +233,27 @@ __device__ __forceinline__ ShardSpan shard_span(int layout, int64_t L, int64_t S
   sp.s0 = 0;
   sp.s1 = Lj < S_max ? Lj : S_max;
   return sp;
+}
+
+// Physical row (index into the cache tensor viewed as rows) of token t of
+// request b, KV head kvh, for a shard with slab index `slab`.  Contiguous and
+// sharded layouts: slab * S_max + t.  Paged: row t mod block_len of block
+// block_table[b, t div block_len] (the id clamped into the pool); rows within
+// one block are consecutive, so any 16-aligned run of 16 tokens (block_len is
+// a power of two >= 16) is 16 consecutive physical rows.
+template <class Args>
+__device__ __forceinline__ int64_t phys_row(const Args& a, int b, int kvh, int64_t slab, int64_t t) {
+  if (a.layout != kPaged) return slab * a.S_max + t;
+  const int64_t lb = t >> a.log2_block;
+  // The table is read-only while a kernel runs: reading it through the
+  // constant address space lets a wave-uniform lookup be a scalar load, which
+  // is waited for on its own counter instead of behind the cache loads in
+  // flight.
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)a.block_table;
+  int64_t pb = table[(int64_t)b * a.max_blocks + lb];
+  pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+  return ((pb * a.Hkv + kvh) << a.log2_block) + (t - (lb << a.log2_block));
 }
 
 // Where global position i lives: shard *j, row *r (contiguous: shard 0, row i).

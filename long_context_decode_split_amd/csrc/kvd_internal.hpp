@@ -23,6 +23,11 @@ struct PartialArgs {
   int32_t v_aliases_k;
   float scale_log2;       // sm_scale * log2(e)
   int32_t layout;         // CacheLayout
+  // paged layout only
+  const int32_t* block_table;   // [B, max_blocks]
+  int32_t log2_block;           // block_len = 1 << log2_block
+  int32_t max_blocks;
+  int64_t num_blocks;
 };
 
 // Arguments of one append (kvd_append_kv), already validated by api.cpp.
@@ -39,6 +44,10 @@ struct AppendArgs {
   int32_t kv_format;
   int32_t v_aliases_k;
   int32_t layout;
+  const int32_t* block_table;
+  int32_t log2_block;
+  int32_t max_blocks;
+  int64_t num_blocks;
 };
 
 // Each family reports whether it handles a problem, then launches it.

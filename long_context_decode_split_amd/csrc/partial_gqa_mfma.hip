@@ -109,8 +109,9 @@ struct Raw {
   uint32_t vs[8];                              // MXFP4: the 4 V block exponents of each token
 };
 
-// VS16 (MXFP4 only): every slab's V scale array is 16-byte aligned.
-template <int KV, bool VS16 = false>
+// VS16 (MXFP4 only): every 16-token run of V scale rows is 16-byte aligned.
+// PAGED: rows are found through the block table (paged cache layout).
+template <int KV, bool VS16, bool PAGED>
 __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   using Lay = Layout<KV>;
   constexpr int64_t ROW = Lay::kRowBytes;
@@ -137,18 +138,30 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   const int64_t bh = (int64_t)b * a.Hkv + kvh;     // fp8 scales are per (request, KV head)
   const int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
 
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + slab * a.S_max * ROW;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + slab * a.S_max * ROW;
-  const uint8_t* ksbase = nullptr;
-  const uint8_t* vsbase = nullptr;
+  // The cache arrays are viewed as rows of ROW bytes (scales: kD/32 bytes).
+  // Contiguous and sharded layouts: token t of this shard is row
+  // slab * S_max + t, so pointers start at the slab; paged: rows come from
+  // the block table (phys_row) and pointers start at the pool.
+  const int64_t row0 = PAGED ? 0 : slab * a.S_max;
+  const uint8_t* kdata = static_cast<const uint8_t*>(a.k) + row0 * ROW;
+  const uint8_t* vdata = static_cast<const uint8_t*>(a.v) + row0 * ROW;
+  const uint8_t* ksdata = nullptr;
+  const uint8_t* vsdata = nullptr;
+  auto hrow = [&](int64_t t) -> int64_t {
+    if constexpr (PAGED) {
+      return phys_row(a, b, kvh, slab, t);
+    } else {
+      return t;
+    }
+  };
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (KV == kFP8) {
     kscale = static_cast<const float*>(a.k_scale)[bh];
     vscale = static_cast<const float*>(a.v_scale)[bh];
   }
   if constexpr (KV == kMXFP4) {
-    ksbase = static_cast<const uint8_t*>(a.k_scale) + slab * a.S_max * (kD / 32);
-    vsbase = static_cast<const uint8_t*>(a.v_scale) + slab * a.S_max * (kD / 32);
+    ksdata = static_cast<const uint8_t*>(a.k_scale) + row0 * (kD / 32);
+    vsdata = static_cast<const uint8_t*>(a.v_scale) + row0 * (kD / 32);
   }
   const float c2 = a.scale_log2 * kscale;  // raw logit -> log2 domain
 
@@ -184,20 +197,28 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   const uint32_t vs_shift = (uint32_t)(8 * (r16 / 4));
 
   // FULL: every row of the tile is inside the shard (no clamping needed).
+  // Each 16-token half-tile is 16 consecutive physical rows starting at
+  // hr[u]; rows of a partial tile are clamped to the shard's last token.
+  constexpr int64_t SROW = kD / 32;   // MXFP4 scale bytes per row
   auto load = [&](Raw<KV>& rw, int tile, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int64_t base = s0 + (int64_t)tile * kTile;
-    const uint8_t* kt = kbase + base * ROW;
-    const uint8_t* vt = vbase + base * ROW;
+    int64_t hr[2] = {0, 0};
+    if constexpr (FULL) {
+      hr[0] = hrow(base);
+      hr[1] = hrow(base + 16);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint8_t* p;
+      int64_t pt = 0;
       if constexpr (FULL) {
-        p = kt + koff + 16 * u * ROW;
+        p = kdata + hr[u] * ROW + koff;
       } else {
         int64_t t = base + 16 * u + r16;
         t = t < last ? t : last;
-        p = kbase + t * ROW + 16 * g;
+        pt = hrow(t);
+        p = kdata + pt * ROW + 16 * g;
       }
 #pragma unroll
       for (int i = 0; i < Lay::kKLoads; ++i) {
@@ -209,11 +230,9 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       }
       if constexpr (KV == kMXFP4) {
         if constexpr (FULL) {
-          rw.ks[u] = stream_load1(ksbase + base * (kD / 32) + ksoff + 16 * u * (kD / 32));
+          rw.ks[u] = stream_load1(ksdata + hr[u] * SROW + ksoff);
         } else {
-          int64_t t = base + 16 * u + r16;
-          t = t < last ? t : last;
-          rw.ks[u] = stream_load1(ksbase + t * (kD / 32) + g);
+          rw.ks[u] = stream_load1(ksdata + pt * SROW + g);
         }
       }
     }
@@ -221,33 +240,31 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if constexpr (FULL && VS16) {
-          const u32x4_t v = stream_load16(vsbase + (base + 16 * u) * (kD / 32) + vsoff);
+          const u32x4_t v = stream_load16(vsdata + hr[u] * SROW + vsoff);
 #pragma unroll
           for (int i = 0; i < 4; ++i) rw.vs[4 * u + i] = v[i];
         } else if constexpr (FULL) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            rw.vs[4 * u + i] = stream_load4(vsbase + (base + 16 * u) * (kD / 32) + vsoff + 4 * i);
+          for (int i = 0; i < 4; ++i) rw.vs[4 * u + i] = stream_load4(vsdata + hr[u] * SROW + vsoff + 4 * i);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             int64_t t = base + 16 * u + 4 * g + i;
             t = t < last ? t : last;
-            rw.vs[4 * u + i] = stream_load4(vsbase + t * (kD / 32));
+            rw.vs[4 * u + i] = stream_load4(vsdata + hrow(t) * SROW);
           }
         }
       }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int erow = 16 * (e / 4) + (e % 4);   // row of token e relative to 4g
       const uint8_t* p;
       if constexpr (FULL) {
-        p = vt + voff + erow * ROW;
+        p = vdata + (hr[e / 4] + (e % 4)) * ROW + voff;   // token 16 (e/4) + 4g + e%4
       } else {
-        int64_t t = base + erow + 4 * g;
+        int64_t t = base + 16 * (e / 4) + (e % 4) + 4 * g;
         t = t < last ? t : last;
-        p = vbase + t * ROW + Lay::kVBytes * r16;
+        p = vdata + hrow(t) * ROW + Lay::kVBytes * r16;
       }
       if constexpr (Lay::kVBytes == 16) {
         const u32x4_t v = stream_load16(p);
@@ -501,20 +518,31 @@ bool gqa_mfma_supports(const PartialArgs& a) {
   return a.kv_format == kBF16 || a.kv_format == kFP8 || a.kv_format == kMXFP4;
 }
 
+template <int KV, bool VS16>
+void launch_gqa(const PartialArgs& a, int64_t blocks, hipStream_t stream) {
+  if (a.layout == kPaged)
+    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+}
+
 hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.kvp * a.B * a.Hkv;
   switch (a.kv_format) {
-    case kBF16:
-      hipLaunchKernelGGL(gqa_mfma_kernel<kBF16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-      break;
-    case kFP8:
-      hipLaunchKernelGGL(gqa_mfma_kernel<kFP8>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-      break;
+    case kBF16: launch_gqa<kBF16, false>(a, blocks, stream); break;
+    case kFP8: launch_gqa<kFP8, false>(a, blocks, stream); break;
     case kMXFP4:
-      if (a.S_max % 4 == 0)
-        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      // 16-token runs of scale rows are 16-byte aligned when every slab
+      // starts at a multiple of 4 rows, and always in a paged pool
+      if (a.layout == kPaged)
+        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, true, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a);
+      else if (a.S_max % 4 == 0)
+        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, true, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a);
       else
-        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, false, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -108,6 +108,8 @@ __device__ __forceinline__ void lds_dma16(uint32_t m0, const uint8_t* sbase, uin
       : "memory");
 }
 
+// PAGED: rows are found through the block table (paged cache layout).
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -129,7 +131,16 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   const int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
   const int64_t last = s1 - 1;
 
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + slab * a.S_max * kRowBytes;
+  // the cache viewed as rows; token t is row t of the slab (contiguous and
+  // sharded layouts) or the row the block table gives (paged)
+  const uint8_t* kdata = static_cast<const uint8_t*>(a.k) + (PAGED ? 0 : slab * a.S_max * kRowBytes);
+  auto hrow = [&](int64_t t) -> int64_t {
+    if constexpr (PAGED) {
+      return phys_row(a, b, kvh, slab, t);
+    } else {
+      return t;
+    }
+  };
   const float c2 = a.scale_log2;
   const int head0 = kvh * kHeads + wave * 32;
 
@@ -165,29 +176,47 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   auto issue = [&](int tile, int buf) {
     const int64_t base = s0 + (int64_t)tile * kTile;
     const uint32_t bufaddr = lds0 + (uint32_t)(buf * kBufBytes);
+    const int64_t g0 = base + kRowsPerWave * wave;   // this wave's first row (8-aligned)
+    if (g0 + kRowsPerWave - 1 <= last) {
+      // all 8 rows inside the shard; an aligned 8-row group is 8 consecutive
+      // physical rows in every layout
+      const uint8_t* src = kdata + hrow(g0) * kRowBytes;
 #pragma unroll
-    for (int k = 0; k < kRowsPerWave; ++k) {
-      const int r = kRowsPerWave * wave + k;
-      int64_t row = base + r;
-      row = row < last ? row : last;
-      lds_dma16(__builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(r * kMainStride * 16)),
-                kbase + row * kRowBytes, (uint32_t)(lane * 16));
-    }
+      for (int k = 0; k < kRowsPerWave; ++k) {
+        const int r = kRowsPerWave * wave + k;
+        lds_dma16(__builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(r * kMainStride * 16)),
+                  src + k * kRowBytes, (uint32_t)(lane * 16));
+      }
 #pragma unroll
-    for (int h = 0; h < kRowsPerWave / 4; ++h) {
-      const int r0 = kRowsPerWave * wave + 4 * h;
-      const uint32_t m0 =
-          __builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(kMainBytes + r0 * kTailStride * 16));
-      const int64_t row0 = base + r0;
-      if (row0 + 3 <= last) {
-        if (lane < 36) lds_dma16(m0, kbase + row0 * kRowBytes, (uint32_t)(tl_row * kRowBytes) + tl_off);
-      } else {
-        // rows clamped per lane, relative to a clamped (in-shard) group base
+      for (int h = 0; h < kRowsPerWave / 4; ++h) {
+        const int r0 = kRowsPerWave * wave + 4 * h;
+        const uint32_t m0 =
+            __builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(kMainBytes + r0 * kTailStride * 16));
+        if (lane < 36) lds_dma16(m0, src + 4 * h * kRowBytes, (uint32_t)(tl_row * kRowBytes) + tl_off);
+      }
+    } else {
+      // last tile: rows clamped to the shard's last token
+#pragma unroll
+      for (int k = 0; k < kRowsPerWave; ++k) {
+        const int r = kRowsPerWave * wave + k;
+        int64_t row = base + r;
+        row = row < last ? row : last;
+        lds_dma16(__builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(r * kMainStride * 16)),
+                  kdata + hrow(row) * kRowBytes, (uint32_t)(lane * 16));
+      }
+#pragma unroll
+      for (int h = 0; h < kRowsPerWave / 4; ++h) {
+        const int r0 = kRowsPerWave * wave + 4 * h;
+        const uint32_t m0 =
+            __builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(kMainBytes + r0 * kTailStride * 16));
+        // rows clamped per lane, relative to a clamped (in-shard) group base;
+        // a 4-aligned group is 4 consecutive physical rows
+        const int64_t row0 = base + r0;
         const int64_t rb = row0 < last ? row0 : last;
         int64_t row = row0 + tl_row;
         row = row < last ? row : last;
         const uint32_t off = (uint32_t)((row - rb) * kRowBytes) + tl_off;
-        if (lane < 36) lds_dma16(m0, kbase + rb * kRowBytes, off);
+        if (lane < 36) lds_dma16(m0, kdata + hrow(rb) * kRowBytes, off);
       }
     }
   };
@@ -397,13 +426,18 @@ bool mla_mfma_supports(const PartialArgs& a) {
 hipError_t launch_partial_mla_mfma(const PartialArgs& a, hipStream_t stream) {
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mla_mfma_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
-    if (e != hipSuccess) return e;
+    for (const void* fn : {reinterpret_cast<const void*>(mla_mfma_kernel<false>),
+                           reinterpret_cast<const void*>(mla_mfma_kernel<true>)}) {
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+      if (e != hipSuccess) return e;
+    }
     configured = true;
   }
   const int64_t blocks = (int64_t)a.kvp * a.B * a.Hkv;
-  hipLaunchKernelGGL(mla_mfma_kernel, dim3((unsigned)blocks), dim3(kThreads), kSmemBytes, stream, a);
+  if (a.layout == kPaged)
+    hipLaunchKernelGGL(mla_mfma_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), kSmemBytes, stream, a);
+  else
+    hipLaunchKernelGGL(mla_mfma_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), kSmemBytes, stream, a);
   return hipGetLastError();
 }
 

@@ -62,9 +62,11 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
   const int64_t slab = span.slab;                  // cache block of this shard
   const int64_t bh = (int64_t)b * a.Hkv + kvh;     // fp8 scales are per (request, KV head)
 
-  const uint8_t* kp = static_cast<const uint8_t*>(a.k) + slab * a.S_max * KROW + li * KLANE;
-  const uint8_t* vp = ALIAS ? static_cast<const uint8_t*>(a.k) + slab * a.S_max * KROW + li * VLANE
-                            : static_cast<const uint8_t*>(a.v) + slab * a.S_max * VROW + li * VLANE;
+  // cache arrays viewed as rows; token t of this shard is physical row
+  // phys_row(t) (slab * S_max + t, or through the block table when paged)
+  const uint8_t* kp = static_cast<const uint8_t*>(a.k) + li * KLANE;
+  const uint8_t* vp = ALIAS ? static_cast<const uint8_t*>(a.k) + li * VLANE
+                            : static_cast<const uint8_t*>(a.v) + li * VLANE;
   const uint8_t* ksp = nullptr;
   const uint8_t* vsp = nullptr;
   float kscale = 1.0f, vscale = 1.0f;
@@ -73,9 +75,9 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
     vscale = ALIAS ? kscale : static_cast<const float*>(a.v_scale)[bh];
   }
   if constexpr (KV == kMXFP4) {
-    ksp = static_cast<const uint8_t*>(a.k_scale) + slab * a.S_max * (DQK / 32) + (li * EK) / 32;
-    vsp = ALIAS ? static_cast<const uint8_t*>(a.k_scale) + slab * a.S_max * (DQK / 32) + (li * EV) / 32
-                : static_cast<const uint8_t*>(a.v_scale) + slab * a.S_max * (DV / 32) + (li * EV) / 32;
+    ksp = static_cast<const uint8_t*>(a.k_scale) + (li * EK) / 32;
+    vsp = ALIAS ? static_cast<const uint8_t*>(a.k_scale) + (li * EV) / 32
+                : static_cast<const uint8_t*>(a.v_scale) + (li * EV) / 32;
   }
   constexpr int64_t KSROW = DQK / 32;
   constexpr int64_t VSROW = ALIAS ? DQK / 32 : DV / 32;
@@ -134,7 +136,8 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
     }
   };
 
-  auto load = [&](int64_t t, uint32_t* kw, uint32_t* vw, float* ks, float* vs) {
+  auto load = [&](int64_t tok, uint32_t* kw, uint32_t* vw, float* ks, float* vs) {
+    const int64_t t = phys_row(a, b, kvh, slab, tok);
     load_dwords<KLANE>(kp + t * KROW, kw);
     load_dwords<VLANE>(vp + t * VROW, vw);
     if constexpr (KV == kMXFP4) {

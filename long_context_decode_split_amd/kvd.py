@@ -24,21 +24,23 @@ LIB_PATH = os.path.join(_HERE, "libkvd.so")
 KVD_OK, KVD_ERR_INVALID, KVD_ERR_UNSUPPORTED, KVD_ERR_HIP = 0, 1, 2, 3
 KVD_F32, KVD_BF16, KVD_FP8_E4M3, KVD_MXFP4 = 0, 1, 2, 3
 DTYPE_CODES = {"f32": KVD_F32, "bf16": KVD_BF16, "fp8": KVD_FP8_E4M3, "mxfp4": KVD_MXFP4}
-KVD_LAYOUT_CONTIGUOUS, KVD_LAYOUT_STRIPED, KVD_LAYOUT_STAGGERED16 = 0, 1, 2
+KVD_LAYOUT_CONTIGUOUS, KVD_LAYOUT_STRIPED, KVD_LAYOUT_STAGGERED16, KVD_LAYOUT_PAGED = 0, 1, 2, 3
 LAYOUT_CODES = {"contiguous": KVD_LAYOUT_CONTIGUOUS, "striped": KVD_LAYOUT_STRIPED,
-                "staggered16": KVD_LAYOUT_STAGGERED16}
+                "staggered16": KVD_LAYOUT_STAGGERED16, "paged": KVD_LAYOUT_PAGED}
 
 # Every symbol include/kvd.h declares.
 EXPORTED = ("kvd_decode_partial", "kvd_lse_merge", "kvd_decode_workspace_bytes", "kvd_decode",
             "kvd_append_kv", "kvd_status_string", "kvd_last_error", "kvd_abi_version")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class KvdProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("S_max", ctypes.c_int64),
                 ("kvp", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("sm_scale", ctypes.c_float), ("v_aliases_k", ctypes.c_int32), ("layout", ctypes.c_int32)]
+                ("sm_scale", ctypes.c_float), ("v_aliases_k", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("block_len", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("num_blocks", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p)]
 
 
 class KvdKV(ctypes.Structure):
@@ -92,14 +94,16 @@ def lib() -> ctypes.CDLL:
 
 
 def problem(B, Hq, Hkv, Dqk, Dv, S_max, kvp, q_dtype, kv_dtype, sm_scale=0.0, v_aliases_k=False,
-            layout="contiguous") -> KvdProblem:
+            layout="contiguous", block_len=0, max_blocks=0, num_blocks=0, block_table=None) -> KvdProblem:
     """A kvd_problem; dtypes may be KVD_* codes or 'f32' / 'bf16' / 'fp8' / 'mxfp4', the layout a
-    KVD_LAYOUT_* code or 'contiguous' / 'striped' / 'staggered16'."""
+    KVD_LAYOUT_* code or 'contiguous' / 'striped' / 'staggered16' / 'paged' (then block_len,
+    max_blocks, num_blocks and the device block_table [B,max_blocks] int32 describe the pool).
+    The problem holds block_table's address: keep the tensor alive while it is used."""
     qd = DTYPE_CODES.get(q_dtype, q_dtype)
     kd = DTYPE_CODES.get(kv_dtype, kv_dtype)
     lay = LAYOUT_CODES.get(layout, layout)
     return KvdProblem(B, Hq, Hkv, Dqk, Dv, S_max, kvp, qd, kd, float(sm_scale), int(bool(v_aliases_k)),
-                      int(lay))
+                      int(lay), int(block_len), int(max_blocks), int(num_blocks), _ptr(block_table))
 
 
 def _ptr(x):

@@ -20,6 +20,14 @@ at which local row):
   "Then reconfigure the same GPUs", staggered KV concatenation: new tokens go
   to one KV-parallel rank for 16 decode steps, then to the next, round-robin).
 
+* ``paged``: a pool of blocks [num_blocks,Hkv,block_len,D]; the cache dict
+  carries "block_table" [B,max_blocks] and "block_len", and token i of
+  request b is row i mod block_len of block block_table[b, i div block_len]
+  (the "Attention DP" design note, section "KV Cache": a per-rank block
+  cache [num_blocks, kv heads, block_len, head dim]; the block table that
+  lists a request's blocks in order is the usual companion of such a pool).
+  Shards are cut by the split rule over positions, as for ``contiguous``.
+
 A sharded cache is [KVP,B,Hkv,S_shard,D] (MXFP4 scales
 [KVP,B,Hkv,S_shard,D/32]); shard j of request b holds its tokens, in
 increasing position, at rows 0 .. L_j - 1.  Decode results do not depend on
@@ -46,7 +54,8 @@ import numpy as np
 
 from .oracle import E2M1_TABLE, E4M3_TABLE, Problem, attend, q_to_f64, slab_kv, split_ranges
 
-LAYOUTS = ("contiguous", "striped", "staggered16")
+LAYOUTS = ("contiguous", "striped", "staggered16")      # by position alone
+PAGED = "paged"
 RUN = 16  # tokens per run of the staggered layout
 
 
@@ -210,6 +219,17 @@ def append(p: Problem, layout: str, kvp: int, cache: dict, positions: Sequence[i
                 row, rsc = encode_row(p.kv_dtype, x[b, kvh, :D], fscale)
                 if i < 0:
                     continue                      # positions outside the cache are skipped
+                if layout == PAGED:
+                    bl, table = cache["block_len"], cache["block_table"]
+                    if i >= table.shape[1] * bl:
+                        continue
+                    pb = int(table[b, i // bl])
+                    if pb < 0 or pb >= data.shape[0]:
+                        continue
+                    data[pb, kvh, i % bl] = row
+                    if p.kv_dtype == "mxfp4":
+                        sc[pb, kvh, i % bl] = rsc
+                    continue
                 if layout == "contiguous":
                     idx = (b, kvh, i)
                     cap = data.shape[2]
@@ -233,6 +253,20 @@ def gather_contiguous(p: Problem, layout: str, kvp: int, cache: dict, seq_lens) 
     if layout == "contiguous":
         return cache
     S = max(1, int(max(seq_lens)))
+    if layout == PAGED:
+        bl, table = cache["block_len"], cache["block_table"]
+        out = {}
+        for name in ("k", "k_scale", "v", "v_scale"):
+            a = cache.get(name)
+            if a is None or (name.endswith("scale") and p.kv_dtype != "mxfp4"):
+                out[name] = a
+                continue
+            g = np.zeros((p.B, p.Hkv, S) + a.shape[3:], dtype=a.dtype)
+            for b in range(p.B):
+                for i in range(int(seq_lens[b])):
+                    g[b, :, i] = a[int(table[b, i // bl]), :, i % bl]
+            out[name] = g
+        return out
     out = {}
     for name in ("k", "k_scale", "v", "v_scale"):
         a = cache.get(name)
@@ -262,9 +296,11 @@ def decode_partials_layout(p: Problem, layout: str, kvp: int, q, cache: dict, se
     """Shard partials o_part [kvp,B,Hq,Dv], lse_part [kvp,B,Hq]: partial j is
     attention over the tokens shard j holds."""
     from .oracle import decode_partials
-    if layout == "contiguous":
-        return decode_partials(p, kvp, q, cache["k"], cache["k_scale"], cache["v"], cache["v_scale"],
-                               seq_lens, pairs)
+    if layout in ("contiguous", PAGED):
+        c = gather_contiguous(p, layout, kvp, cache, seq_lens)
+        pc = Problem(p.B, p.Hq, p.Hkv, p.Dqk, p.Dv, c["k"].shape[2], p.q_dtype, p.kv_dtype, p.v_aliases_k,
+                     p.sm_scale)
+        return decode_partials(pc, kvp, q, c["k"], c["k_scale"], c["v"], c["v_scale"], seq_lens, pairs)
     qf = q_to_f64(q, p.q_dtype)
     o = np.full((kvp, p.B, p.Hq, p.Dv), np.nan)
     lse = np.full((kvp, p.B, p.Hq), np.nan)

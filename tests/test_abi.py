@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvd.kvd_abi_version() == kvd.ABI_VERSION == 2
+    assert kvd.kvd_abi_version() == kvd.ABI_VERSION == 3
     for s in range(4):
         assert kvd.kvd_status_string(s).startswith(("KVD_OK", "KVD_ERR"))
     assert "unknown" in kvd.kvd_status_string(99)
@@ -170,3 +170,15 @@ def test_append_alias_and_problem_rules():
     assert call_append(p, k=(FAKE, None), v=(None, None)) == INV          # v_new must be NULL
     assert call_append(good_problem(layout=7)) == INV
     assert call_append(good_problem(B=0)) == INV
+
+
+@pytest.mark.parametrize("kw", [
+    dict(block_len=8), dict(block_len=24), dict(block_len=0), dict(block_len=1 << 21),
+    dict(max_blocks=0), dict(num_blocks=0), dict(block_table=None), dict(block_table=FAKE + 2),
+])
+def test_paged_problem_validation(kw):
+    base = dict(layout="paged", block_len=16, max_blocks=8, num_blocks=32, block_table=FAKE)
+    base.update(kw)
+    assert call_partial(good_problem(**base)) == INV
+    assert call_append(good_problem(**base)) == INV
+    assert kvd.kvd_decode_workspace_bytes(good_problem(**base)) == 0

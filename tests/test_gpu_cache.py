@@ -201,3 +201,100 @@ def test_decode_loop_appends_one_token_per_step(layout):
         torch.cuda.synchronize()
         ref_o, ref_l = oc.decode_layout(po, layout, kvp, q, host, L)
         gc.compare(o.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "fp8", "%s step %d" % (layout, step))
+
+
+def _paged_from_contiguous(w, inp, bl, max_blocks, rng, spare=5):
+    """Scatter a generated contiguous cache [B,Hkv,max_blocks*bl,...] into a
+    pool of blocks through a scrambled block table."""
+    num_blocks = w.B * max_blocks + spare
+    table = rng.permutation(num_blocks)[:w.B * max_blocks].reshape(w.B, max_blocks).astype(np.int32)
+    def scatter(a):
+        if a is None:
+            return None
+        pool = np.zeros((num_blocks, w.Hkv, bl) + a.shape[3:], dtype=a.dtype)
+        for b in range(w.B):
+            for lb in range(max_blocks):
+                pool[table[b, lb]] = a[b, :, lb * bl:(lb + 1) * bl]
+        return pool
+    cache = {"k": scatter(inp.k_data), "v": scatter(inp.v_data), "block_len": bl, "block_table": table}
+    if w.kv_dtype == "mxfp4":
+        cache["k_scale"], cache["v_scale"] = scatter(inp.k_scale), scatter(inp.v_scale)
+    else:
+        cache["k_scale"], cache["v_scale"] = inp.k_scale, inp.v_scale
+    return cache, num_blocks
+
+
+def _paged_problem(w, kvp, cache, num_blocks, table_dev):
+    from long_context_decode_split_amd import kvd
+    return kvd.problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, 1, kvp, w.q_dtype, w.kv_dtype, 0.0, w.v_aliases_k,
+                       layout="paged", block_len=cache["block_len"], max_blocks=cache["block_table"].shape[1],
+                       num_blocks=num_blocks, block_table=table_dev)
+
+
+PAGED_CASES = [(kv, sh, bl) for kv in ("bf16", "fp8", "mxfp4") for sh in ("g16", "g4", "mla") for bl in (16, 64)
+               if not (sh == "mla" and kv != "bf16") and not (sh == "g4" and kv == "mxfp4")]
+
+
+@pytest.mark.parametrize("kv,shape,bl", PAGED_CASES, ids=lambda x: str(x))
+def test_decode_paged(kv, shape, bl):
+    """Partials and merged output over a paged pool with a scrambled block
+    table, ragged lengths, an empty request and a full table."""
+    import torch
+    from long_context_decode_split_amd import kvd
+    max_blocks = 192 // bl
+    S = max_blocks * bl
+    w = _wl(kv, S=S, **SHAPES[shape])
+    inp = kvgen.make_inputs(w)
+    rng = np.random.default_rng(bl)
+    cache, num_blocks = _paged_from_contiguous(w, inp, bl, max_blocks, rng)
+    table_dev = _dev(cache["block_table"])
+    p = _paged_problem(w, 5, cache, num_blocks, table_dev)
+    po = oracle.Problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, S, w.q_dtype, w.kv_dtype, w.v_aliases_k)
+    k = (_dev(cache["k"]), _dev(cache["k_scale"]))
+    v = None if w.v_aliases_k else (_dev(cache["v"]), _dev(cache["v_scale"]))
+    f32 = dict(dtype=torch.float32, device="cuda")
+    for seq in ((S, 0), (177, 31), (bl + 1, S - 3)):
+        o_part = torch.full((5, w.B, w.Hq, w.Dv), float("nan"), **f32)
+        lse_part = torch.full((5, w.B, w.Hq), float("nan"), **f32)
+        seq_d = _dev(np.asarray(seq, dtype=np.int32))
+        kvd.kvd_decode_partial(p, _dev(inp.q), k, v, seq_d, o_part, lse_part)
+        torch.cuda.synchronize()
+        ref_po, ref_pl = oc.decode_partials_layout(po, "paged", 5, inp.q, cache, np.array(seq))
+        gc.compare(o_part.cpu().numpy(), lse_part.cpu().numpy(), ref_po, ref_pl, kv,
+                   "paged bl=%d %s %s L=%s" % (bl, kv, shape, seq))
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8", "mxfp4"])
+def test_append_paged_bitexact(kv):
+    import torch
+    from long_context_decode_split_amd import kvd
+    bl, max_blocks, T = 16, 4, 70
+    w = _wl(kv, B=3, Hq=8, Hkv=2, D=64 if kv != "mxfp4" else 128, S=bl * max_blocks)
+    rng = np.random.default_rng(12)
+    num_blocks = w.B * max_blocks + 2
+    table = rng.permutation(num_blocks)[:w.B * max_blocks].reshape(w.B, max_blocks).astype(np.int32)
+    table[2, 1] = -1                                   # writes through it are skipped
+    zero = _zero_cache(w, "contiguous", 1, 1)
+    def pool(a):
+        return None if a is None else np.zeros((num_blocks, w.Hkv, bl) + a.shape[3:], a.dtype)
+    host = {"k": pool(zero["k"]), "v": pool(zero["v"]), "block_len": bl, "block_table": table}
+    if kv == "mxfp4":
+        host["k_scale"], host["v_scale"] = pool(zero["k_scale"]), pool(zero["v_scale"])
+    else:
+        host["k_scale"], host["v_scale"] = zero["k_scale"], zero["v_scale"]
+    dev = {n: _dev(host[n]) for n in ("k", "k_scale", "v", "v_scale")}
+    table_dev = _dev(table)
+    p = kvd.problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, 1, 2, w.q_dtype, w.kv_dtype, 0.0, False, layout="paged",
+                    block_len=bl, max_blocks=max_blocks, num_blocks=num_blocks, block_table=table_dev)
+    po = oracle.Problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, bl * max_blocks, w.q_dtype, w.kv_dtype)
+    for t in range(T):
+        kn = rng.standard_normal((w.B, w.Hkv, w.Dqk)).astype(np.float32)
+        vn = rng.standard_normal((w.B, w.Hkv, w.Dv)).astype(np.float32)
+        pos = np.array([t, (3 * t) % (bl * max_blocks + 5), t // 2], dtype=np.int32)
+        oc.append(po, "paged", 2, host, pos, kn, vn)
+        kvd.kvd_append_kv(p, _dev(kn), _dev(vn), _dev(pos), (dev["k"], dev["k_scale"]), (dev["v"], dev["v_scale"]))
+    torch.cuda.synchronize()
+    for n in ("k", "v"):
+        assert np.array_equal(_host(dev[n], host[n]).view(np.uint8), host[n].view(np.uint8)), n
+        if kv == "mxfp4":
+            assert np.array_equal(_host(dev[n + "_scale"], host[n + "_scale"]), host[n + "_scale"]), n

@@ -224,3 +224,61 @@ def test_append_latent_alias_writes_k_only():
     assert sh["v"] is None
     assert np.all(sh["k"][1, 0, 0, 1] == 0x3F80)     # position 3 -> shard 1, row 1
     assert np.all(sh["k"][0, 1, 0, 0] == 0x3F80)     # position 0 -> shard 0, row 0
+
+
+def _paged_cache(p, num_blocks, bl, table):
+    def one(D):
+        if p.kv_dtype == "f32":
+            return np.zeros((num_blocks, p.Hkv, bl, D), np.float32), None
+        if p.kv_dtype == "bf16":
+            return np.zeros((num_blocks, p.Hkv, bl, D), np.uint16), None
+        if p.kv_dtype == "fp8":
+            return np.zeros((num_blocks, p.Hkv, bl, D), np.uint8), np.full((p.B, p.Hkv), 0.05, np.float32)
+        return (np.zeros((num_blocks, p.Hkv, bl, D // 2), np.uint8),
+                np.zeros((num_blocks, p.Hkv, bl, D // 32), np.uint8))
+    k, ks = one(p.Dqk)
+    v, vs = one(p.Dv)
+    return {"k": k, "k_scale": ks, "v": v, "v_scale": vs, "block_len": bl, "block_table": table}
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
+def test_paged_appends_then_decode_equal_contiguous(kv):
+    """A paged pool with a scrambled block table holds, after the same appends,
+    the rows of a contiguous cache at the blocks the table names; decode and
+    shard partials agree; positions past the table and negative block ids are
+    skipped."""
+    p = _problem(kv, D=64 if kv != "mxfp4" else 128)
+    bl, max_blocks, T, kvp = 16, 5, 75, 3
+    rng = np.random.default_rng(8)
+    num_blocks = p.B * max_blocks + 3
+    table = rng.permutation(num_blocks)[:p.B * max_blocks].reshape(p.B, max_blocks).astype(np.int32)
+    pg = _paged_cache(p, num_blocks, bl, table)
+    co = _alloc(p, "contiguous", 1, max_blocks * bl)
+    if kv == "fp8":
+        pg["v_scale"][:] = co["v_scale"][:] = 0.03
+    for t in range(T):
+        kn = rng.standard_normal((p.B, p.Hkv, p.Dqk)).astype(np.float32)
+        vn = rng.standard_normal((p.B, p.Hkv, p.Dv)).astype(np.float32)
+        oc.append(p, "paged", kvp, pg, [t, t], kn, vn)
+        oc.append(p, "contiguous", kvp, co, [t, t], kn, vn)
+    for b in range(p.B):
+        for i in range(T):
+            assert np.array_equal(pg["k"][table[b, i // bl], :, i % bl], co["k"][b, :, i])
+    seq = np.array([T, 33], dtype=np.int32)
+    q = rng.standard_normal((p.B, p.Hq, p.Dqk)).astype(np.float32)
+    pc = oracle.Problem(p.B, p.Hq, p.Hkv, p.Dqk, p.Dv, max_blocks * bl, "f32", kv)
+    ref = oracle.decode(pc, q, co["k"], co["k_scale"], co["v"], co["v_scale"], seq)
+    got = oc.decode_layout(p, "paged", kvp, q, pg, seq)
+    np.testing.assert_allclose(got[0], ref[0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(got[1], ref[1], rtol=0, atol=1e-13)
+    rpo, rpl = oracle.decode_partials(pc, kvp, q, co["k"], co["k_scale"], co["v"], co["v_scale"], seq)
+    po, pl = oc.decode_partials_layout(p, "paged", kvp, q, pg, seq)
+    np.testing.assert_allclose(po, rpo, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(pl, rpl, rtol=0, atol=1e-13)
+    # skipped writes: past the table, and through a negative block id
+    before = pg["k"].copy()
+    pg["block_table"] = table.copy()
+    pg["block_table"][1, 0] = -1
+    oc.append(p, "paged", kvp, pg, [max_blocks * bl, 3], np.ones((p.B, p.Hkv, p.Dqk), np.float32),
+              np.ones((p.B, p.Hkv, p.Dv), np.float32))
+    assert np.array_equal(pg["k"], before)

@@ -13,7 +13,8 @@ from tests import test_oracle_cache as pins
 
 _REAL_E4M3 = oc.encode_e4m3
 _REAL = {n: getattr(oc, n) for n in ("owner", "_nearest_code", "encode_bf16", "mxfp4_block_exponent",
-                                     "encode_fp8", "encode_mxfp4_row", "decode_partials_layout")}
+                                     "encode_fp8", "encode_mxfp4_row", "decode_partials_layout",
+                                     "gather_contiguous")}
 
 
 def _owner_staggered_local_wrong(i, kvp, layout):
@@ -65,6 +66,24 @@ def _partials_rotated(p, layout, kvp, q, cache, seq_lens, pairs=None):
     return np.roll(o, 1, axis=0), np.roll(l, 1, axis=0)
 
 
+def _gather_paged_row_block_swapped(p, layout, kvp, cache, seq_lens):
+    if layout != "paged":
+        return _REAL["gather_contiguous"](p, layout, kvp, cache, seq_lens)
+    c = dict(cache)
+    bl, table = cache["block_len"], cache["block_table"]
+    S = max(1, int(max(seq_lens)))
+    for name in ("k", "v"):
+        a = cache[name]
+        g = np.zeros((p.B, p.Hkv, S) + a.shape[3:], dtype=a.dtype)
+        for b in range(p.B):
+            for i in range(int(seq_lens[b])):
+                g[b, :, i] = a[int(table[b, i % table.shape[1]]), :, (i // table.shape[1]) % bl]
+        c[name] = g
+    for name in ("k_scale", "v_scale"):
+        c[name] = _REAL["gather_contiguous"](p, layout, kvp, cache, seq_lens)[name]
+    return c
+
+
 MUTATIONS = {
     "staggered: local row i div kvp": ("owner", _owner_staggered_local_wrong),
     "striped: shard (i div kvp) mod kvp": ("owner", _owner_striped_shard_wrong),
@@ -75,6 +94,7 @@ MUTATIONS = {
     "fp8: overflow encodes NaN instead of saturating": ("encode_e4m3", _e4m3_overflow_to_nan),
     "mxfp4: nibbles swapped": ("encode_mxfp4_row", _mx_nibbles_swapped),
     "partials: shard outputs rotated": ("decode_partials_layout", _partials_rotated),
+    "paged: block and row indices interleaved": ("gather_contiguous", _gather_paged_row_block_swapped),
 }
 
 
