@@ -165,6 +165,7 @@ class Workload:
     seed: int
     seq_lens: object = None
     v_aliases_k: bool = False
+    q_tokens: int = 1          # new query tokens per request (T)
 
     @property
     def G(self) -> int:
@@ -215,7 +216,8 @@ WORKLOADS = {
 class Inputs:
     """Encoded host-side inputs in the library's layouts.
 
-    q        [B,Hq,Dqk]       float32, or uint16 bf16 bit patterns
+    q        [B,Hq,Dqk] ([B,T,Hq,Dqk] for T > 1 query tokens) float32, or
+             uint16 bf16 bit patterns
     k_data   [B,Hkv,S_max,D]  float32 / uint16 (bf16) / uint8 (fp8 codes);
              MXFP4: uint8 [B,Hkv,S_max,D/2], element 2i in the low nibble
     k_scale  fp8: float32 [B,Hkv]; MXFP4: uint8 E8M0 [B,Hkv,S_max,D/32]; else None
@@ -243,11 +245,15 @@ def gen_seq_lens(w: Workload) -> np.ndarray:
 
 
 def gen_q(w: Workload, threads=None) -> np.ndarray:
-    n = w.B * w.Hq * w.Dqk
+    """q [B,Hq,Dqk] for one query token, [B,T,Hq,Dqk] for T = q_tokens > 1
+    (the same flat stream, so a T = 1 query is the first token's)."""
+    T = w.q_tokens
+    shape = (w.B, w.Hq, w.Dqk) if T == 1 else (w.B, T, w.Hq, w.Dqk)
+    n = w.B * T * w.Hq * w.Dqk
     if w.q_dtype == "f32":
-        return normals_f32(w.seed, STREAM_Q, 0, n, threads).reshape(w.B, w.Hq, w.Dqk)
+        return normals_f32(w.seed, STREAM_Q, 0, n, threads).reshape(shape)
     if w.q_dtype == "bf16":
-        return normals_bf16(w.seed, STREAM_Q, 0, n, threads).reshape(w.B, w.Hq, w.Dqk)
+        return normals_bf16(w.seed, STREAM_Q, 0, n, threads).reshape(shape)
     raise ValueError(w.q_dtype)
 
 
