@@ -33,14 +33,14 @@ METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S
 
 # HBM bytes per launch of the partial kernel measured with rocprofv3 counters
 # (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a plain 1 GiB
-# copy), keyed by (workload, cache layout, kvp, sha256 prefix of the kernel code the
+# copy), keyed by (workload, cache layout, kvp, query tokens, sha256 prefix of the kernel code the
 # counters were taken on).  Changed kernel code no longer matches, and the
 # bench then reports traffic as null.  Summaries are under profiles/.
 TRAFFIC = {
-    ("helix_fp8", "contiguous", 32, "b385f0b82e79652f"): 17529276368,
-    ("helix_mxfp4", "contiguous", 32, "b385f0b82e79652f"): 9182880567,
-    ("gqa_bf16_varlen", "contiguous", 16, "b385f0b82e79652f"): 3475220072,
-    ("mla_bf16", "contiguous", 32, "5a82cc7521779442"): 4900503907,
+    ("helix_fp8", "contiguous", 32, 1, "b385f0b82e79652f"): 17529276368,
+    ("helix_mxfp4", "contiguous", 32, 1, "b385f0b82e79652f"): 9182880567,
+    ("gqa_bf16_varlen", "contiguous", 16, 1, "b385f0b82e79652f"): 3475220072,
+    ("mla_bf16", "contiguous", 32, 1, "5a82cc7521779442"): 4900503907,
 }
 KERNEL_SOURCES = {"bf16": "partial_gqa_mfma.hip", "fp8": "partial_gqa_mfma.hip",
                   "mxfp4": "partial_gqa_mfma.hip", "f32": "partial_valu.hip"}
@@ -86,7 +86,8 @@ def cpu_baseline(w, target_s=15.0):
     except Exception:  # noqa: BLE001
         blas_threads = 1
     cores = len(os.sched_getaffinity(0))
-    q = kvgen.gen_q(w)
+    T = w.q_tokens
+    q = kvgen.gen_q(w).reshape(w.B, T, w.Hq, w.Dqk)
     seq = kvgen.gen_seq_lens(w)
     p = oracle.Problem.from_workload(w)
     G = w.G
@@ -103,8 +104,11 @@ def cpu_baseline(w, target_s=15.0):
         else:
             k = oracle.dequant(w.kv_dtype, kd[:L], ks, w.Dqk)
             v = k[:, :w.Dv] if w.v_aliases_k else oracle.dequant(w.kv_dtype, vd[:L], vs, w.Dv)
-        qf = oracle.q_to_f64(q[b, kvh * G:(kvh + 1) * G], w.q_dtype)
-        oracle.attend(qf, k, v, p.sm_scale)
+        for t in range(T):
+            # query t sees the first L - T + 1 + t tokens (causal among new tokens)
+            n = max(0, min(L, L - T + 1 + t))
+            qf = oracle.q_to_f64(q[b, t, kvh * G:(kvh + 1) * G], w.q_dtype)
+            oracle.attend(qf, k[:n], v[:n], p.sm_scale)
         elapsed += time.perf_counter() - t0
         done_bytes += roofline.kv_bytes(1, [L], w.Dqk, w.Dv, w.kv_dtype, w.v_aliases_k)
         slabs += 1
@@ -113,8 +117,8 @@ def cpu_baseline(w, target_s=15.0):
             break
     return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": int(max(cores, blas_threads)),
             "blas_threads": int(blas_threads), "host_cpus": int(cores), "kind": "oracle",
-            "sample": "%d of %d (request, KV head) slabs of %s, full length each, float64 dequant + "
-                      "attention, %.1f s" % (slabs, len(pairs), w.name, elapsed),
+            "sample": "%d of %d (request, KV head) slabs of %s, full length each, %d query token(s), "
+                      "float64 dequant + attention, %.1f s" % (slabs, len(pairs), w.name, T, elapsed),
             "seconds": elapsed, "bytes": int(done_bytes)}
 
 
@@ -130,6 +134,9 @@ def main():
                          "S/kvp rows, the paged layout as a pool of blocks handed to the requests in "
                          "a seeded random order (same bytes, same per-step traffic)")
     ap.add_argument("--block-len", type=int, default=16, help="tokens per block of the paged layout")
+    ap.add_argument("--q-tokens", type=int, default=1,
+                    help="query tokens per request (a multi-token turn, causal among the new tokens; "
+                         "the cache's last T tokens are the new ones)")
     ap.add_argument("--no-append", action="store_true", help="skip timing kvd_append_kv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -161,7 +168,8 @@ def main():
     from kvgen.device import generate_on_device
     from long_context_decode_split_amd import kvd, roofline
 
-    w = kvgen.WORKLOADS[args.workload]
+    T = args.q_tokens
+    w = kvgen.WORKLOADS[args.workload].with_(q_tokens=T)
     kvp = args.kvp or (32 if 32 in w.kvp else w.kvp[0])
     torch.cuda.set_device(0)
     log("generating %s (kvp=%d) into device memory" % (w.name, kvp))
@@ -204,17 +212,17 @@ def main():
         if dev.v is not None:
             dev.v = (shard_view(dev.v[0], True), shard_view(dev.v[1], mx))
     p = kvd.problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, S_cache, kvp, w.q_dtype, w.kv_dtype, 0.0, w.v_aliases_k,
-                    layout=args.layout, **paging)
+                    layout=args.layout, q_tokens=T, **paging)
     f32 = dict(dtype=torch.float32, device="cuda")
-    o_part = torch.empty((kvp, w.B, w.Hq, w.Dv), **f32)
-    lse_part = torch.empty((kvp, w.B, w.Hq), **f32)
-    o = torch.empty((w.B, w.Hq, w.Dv), **f32)
-    lse = torch.empty((w.B, w.Hq), **f32)
-    rows = w.B * w.Hq
+    o_part = torch.empty((kvp, w.B, T, w.Hq, w.Dv), **f32)
+    lse_part = torch.empty((kvp, w.B, T, w.Hq), **f32)
+    o = torch.empty((w.B, T, w.Hq, w.Dv), **f32)
+    lse = torch.empty((w.B, T, w.Hq), **f32)
+    rows = w.B * T * w.Hq
     stream = torch.cuda.Stream()
     seq = dev.seq_lens.cpu().numpy()
     kv_bytes = roofline.kv_bytes(w.Hkv, seq, w.Dqk, w.Dv, w.kv_dtype, w.v_aliases_k)
-    flops = roofline.attention_flops(w.Hq, seq, w.Dqk, w.Dv)
+    flops = roofline.attention_flops_tokens(w.Hq, seq, T, w.Dqk, w.Dv)
 
     def step(ev0=None, ev1=None, ev2=None):
         if ev0 is not None:
@@ -251,7 +259,7 @@ def main():
     achieved = kv_bytes / (partial_avg * 1e-3) / 1e9
     peak = roofline.HBM_BYTES_PER_S / 1e9
     khash = kernel_hash(w.kv_dtype, mla=w.v_aliases_k)
-    traffic = TRAFFIC.get((w.name, args.layout, kvp, khash))
+    traffic = TRAFFIC.get((w.name, args.layout, kvp, T, khash))
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -271,7 +279,7 @@ def main():
         "data": "synthetic (seeded N(0,1), encoded to the cache format)",
         "config": {"workload": w.name, "layout": args.layout,
                    "block_len": args.block_len if args.layout == "paged" else None, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Hsz": w.Dqk, "Dv": w.Dv,
-                   "S": w.S_max, "kvp": kvp, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
+                   "S": w.S_max, "kvp": kvp, "q_tokens": T, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
                    "kv_bytes": kv_bytes, "flops": flops},
         "partial_us": round(partial_avg * 1e3, 2),
         "partial_us_median": round(median(partial_ms) * 1e3, 2),
@@ -285,12 +293,20 @@ def main():
                      "bytes_per_launch": kv_bytes,
                      "tflops": round(flops / (partial_avg * 1e-3) / 1e12, 2)},
     }
+    # With several query tokens the same bytes feed T times the arithmetic:
+    # the pass is bound by whichever ideal time is longer.
+    fpeak = roofline.VALU_FP32_FLOPS if w.kv_dtype == "f32" else roofline.MFMA_BF16_FLOPS
+    if flops / fpeak > kv_bytes / roofline.HBM_BYTES_PER_S:
+        ach = flops / (partial_avg * 1e-3) / 1e12
+        res["roofline"].update({"bound": "alu" if w.kv_dtype == "f32" else "mfma", "achieved": round(ach, 2),
+                                "peak": fpeak / 1e12, "unit": "TFLOP/s", "frac": round(ach / (fpeak / 1e12), 4),
+                                "flops_per_launch": flops, "hbm_frac": round(achieved / peak, 4)})
     if not args.no_append:
-        # one decode step's KV write: a new fp32 token row per (request, KV head),
-        # appended at the last position of every request
-        kn = torch.randn((w.B, w.Hkv, w.Dqk), dtype=torch.float32, device="cuda")
-        vn = None if w.v_aliases_k else torch.randn((w.B, w.Hkv, w.Dv), dtype=torch.float32, device="cuda")
-        pos = torch.full((w.B,), w.S_max - 1, dtype=torch.int32, device="cuda")
+        # one step's KV write: T new fp32 token rows per (request, KV head),
+        # appended at the last T positions of every request
+        kn = torch.randn((w.B, T, w.Hkv, w.Dqk), dtype=torch.float32, device="cuda")
+        vn = None if w.v_aliases_k else torch.randn((w.B, T, w.Hkv, w.Dv), dtype=torch.float32, device="cuda")
+        pos = torch.full((w.B,), w.S_max - T, dtype=torch.int32, device="cuda")
         app = []
         with torch.cuda.stream(stream):
             for i in range(args.warmup + args.steps):

@@ -11,6 +11,16 @@
  * KV head; multi-head latent attention is the case Hkv = 1 with V the first Dv
  * columns of the cached latent K.
  *
+ * Several query tokens (q_tokens = T > 1).  A turn that brings T new tokens
+ * to a request (the pass-Q setting of the "Context Parallelism for Scalable
+ * Million-Token Inference" note, section "A runtime heuristic chooses the
+ * ring direction": Q is [T, N_H, D_H] while K and V are [T + P, N_KV, D_H],
+ * so the new tokens' keys and values are in the cache, appended first) has
+ * query token t at position L - T + t, and attention among the new tokens is
+ * causal: query t attends to positions 0 .. L - T + t, i.e. the sum over s
+ * above stops at L - T + t.  A query with no such position (L < T - t)
+ * yields o = 0, lse = -inf.  T = 1 is the single-token decode.
+ *
  * The split.  Following KV parallelism in "Helix Parallelism: Why Tensor
  * Parallelism Hits a Wall at Million-Token Context" (section "Sharding the
  * sequence instead"), the sequence of each request is cut into kvp shards;
@@ -31,10 +41,10 @@
  *    synchronizes; it keeps no state between calls and is reentrant.
  *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the null
  *    stream) and the call returns without waiting for it.
- *  - Layouts: contiguous row-major.  q [B,Hq,Dqk]; k.data [B,Hkv,S_max,Dqk];
+ *  - Layouts: contiguous row-major.  q [B,T,Hq,Dqk]; k.data [B,Hkv,S_max,Dqk];
  *    v.data [B,Hkv,S_max,Dv]; seq_lens int32 [B]; outputs are fp32:
- *    o [B,Hq,Dv], lse [B,Hq] (natural log), o_part [kvp,B,Hq,Dv],
- *    lse_part [kvp,B,Hq].
+ *    o [B,T,Hq,Dv], lse [B,T,Hq] (natural log), o_part [kvp,B,T,Hq,Dv],
+ *    lse_part [kvp,B,T,Hq] (T = 1: the [B,Hq,...] arrays of one token).
  *  - KV formats (kv_dtype):
  *      KVD_F32, KVD_BF16: plain elements; scale must be NULL.
  *      KVD_FP8_E4M3: OCP E4M3 ("fn") codes, one byte per element; scale is a
@@ -90,7 +100,8 @@
  * [16, 2^20], S_max is not used, lengths are clamped to max_blocks *
  * block_len and block ids into [0, num_blocks).  Decode results do not
  * depend on the layout; shard j's partial is attention over the tokens shard
- * j holds.
+ * j holds (for query token t: those at positions up to L - T + t, which are
+ * the first rows of the shard).
  */
 #ifndef KVD_H_
 #define KVD_H_
@@ -102,7 +113,7 @@
 extern "C" {
 #endif
 
-#define KVD_ABI_VERSION 3
+#define KVD_ABI_VERSION 4
 
 typedef enum {
   KVD_OK = 0,
@@ -150,6 +161,8 @@ typedef struct {
   int32_t max_blocks;   /* KVD_LAYOUT_PAGED only: columns of block_table */
   int64_t num_blocks;   /* KVD_LAYOUT_PAGED only: blocks in the pool */
   const int32_t* block_table;  /* KVD_LAYOUT_PAGED only: device [B,max_blocks] */
+  int32_t q_tokens;     /* T, query tokens per request (and new tokens per
+                           request for kvd_append_kv), 0 .. 65536; 0 means 1 */
 } kvd_problem;
 
 /* One cache tensor: element data and, for fp8 / MXFP4, its scales. */
@@ -158,10 +171,11 @@ typedef struct {
   const void* scale;
 } kvd_kv;
 
-/* Shard partials: for every request b, shard j < kvp and query head h,
- * o_part[j,b,h,:] = softmax-weighted mean of V over shard j's tokens (fp32)
- * and lse_part[j,b,h] = ln sum over shard j of exp(x_s) (fp32), i.e. the
- * (o_local, lse_local) pair each KV-parallel rank produces. */
+/* Shard partials: for every request b, shard j < kvp, query token t and
+ * query head h, o_part[j,b,t,h,:] = softmax-weighted mean of V over the tokens
+ * of shard j that query t sees (fp32) and lse_part[j,b,t,h] = ln sum of
+ * exp(x_s) over them (fp32), i.e. the (o_local, lse_local) pair each
+ * KV-parallel rank produces. */
 int kvd_decode_partial(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
                        const int32_t* seq_lens, float* o_part, float* lse_part,
                        kvd_stream_t stream);
@@ -178,18 +192,19 @@ int kvd_lse_merge(int32_t kvp, int64_t rows, int32_t Dv, const float* o_part,
  * partials, 256-byte aligned pieces); 0 if p is invalid. */
 size_t kvd_decode_workspace_bytes(const kvd_problem* p);
 
-/* kvd_decode_partial into `workspace` followed by kvd_lse_merge into o, lse,
- * both on `stream`: the exact full-context result. */
+/* kvd_decode_partial into `workspace` followed by kvd_lse_merge (rows =
+ * B*T*Hq) into o, lse, both on `stream`: the exact full-context result. */
 int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
                const int32_t* seq_lens, void* workspace, float* o, float* lse,
                kvd_stream_t stream);
 
-/* Append one new token per request to the cache (the decode step's KV
- * write).  For every request b and KV head kvh, the fp32 row k_new[b,kvh,:]
- * (Dqk values) and v_new[b,kvh,:] (Dv values) are encoded to kv_dtype and
- * stored at global position positions[b] under p->layout (contiguous: row
- * positions[b]; sharded: the owner shard's local row; paged: the row of the
- * position's block in the block table).  Encodings:
+/* Append T = q_tokens new tokens per request to the cache (the decode step's
+ * KV write, or the new tokens of a multi-token turn).  For every request b,
+ * token t and KV head kvh, the fp32 rows k_new[b,t,kvh,:] (Dqk values) and
+ * v_new[b,t,kvh,:] (Dv values) are encoded to kv_dtype and stored at global
+ * position positions[b] + t under p->layout (contiguous: that row; sharded:
+ * the owner shard's local row; paged: the row of the position's block in the
+ * block table).  Encodings:
  *   KVD_F32: copied.  KVD_BF16: round to nearest, ties to even.
  *   KVD_FP8_E4M3: y = x / scale[b,kvh] in fp32 (the slab's existing scale,
  *     read, not changed), then the nearest E4M3 value, ties to even,
@@ -198,12 +213,13 @@ int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
  *     0, 254) (127 for an all-zero block), written to the row's scale bytes;
  *     each element x * 2^(127 - E) becomes the nearest E2M1 value, ties to
  *     even, saturated to +-6 (OCP MX).
- * k_new [B,Hkv,Dqk] and v_new [B,Hkv,Dv] are fp32 device arrays of finite
+ * k_new [B,T,Hkv,Dqk] and v_new [B,T,Hkv,Dv] are fp32 device arrays of finite
  * values, 4-byte aligned; v_new must be NULL when V aliases K.  positions is
- * an int32 [B] device array; a position that is negative, or whose row falls
- * outside the cache (contiguous: >= S_max; sharded: local row >= S_max;
- * paged: position >= max_blocks * block_len or a block id outside
- * [0, num_blocks)), is skipped on the device.  k and v are the cache tensors of kvd_decode_partial
+ * an int32 [B] device array; a request whose positions[b] is negative is
+ * skipped, and so is each token whose row falls outside the cache
+ * (contiguous: >= S_max; sharded: local row >= S_max; paged: position >=
+ * max_blocks * block_len or a block id outside [0, num_blocks)).  Tokens of
+ * one call must not share a row (positions[b] + t distinct per request).  k and v are the cache tensors of kvd_decode_partial
  * (written through their const pointers).  kvp and layout of p define the
  * map; q_dtype and sm_scale are ignored. */
 int kvd_append_kv(const kvd_problem* p, const float* k_new, const float* v_new,

@@ -33,6 +33,7 @@ int ok() {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int kMaxKvp = 4096;
+constexpr int kMaxQTokens = 65536;
 constexpr size_t kWorkspaceAlign = 256;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -48,6 +49,9 @@ int elem_bits(int kv) {
   }
 }
 
+// Query (and new) tokens per request: q_tokens, with 0 meaning 1.
+int64_t tokens(const kvd_problem* p) { return p->q_tokens == 0 ? 1 : p->q_tokens; }
+
 // Shape and format checks shared by every entry point taking a kvd_problem.
 int check_problem(const kvd_problem* p) {
   if (p == nullptr) return fail(KVD_ERR_INVALID, "problem is NULL");
@@ -61,6 +65,8 @@ int check_problem(const kvd_problem* p) {
     return fail(KVD_ERR_INVALID, "kvp must be in [1, %d] (got %d)", kMaxKvp, p->kvp);
   if (p->q_dtype != KVD_F32 && p->q_dtype != KVD_BF16)
     return fail(KVD_ERR_INVALID, "q_dtype must be KVD_F32 or KVD_BF16");
+  if (p->q_tokens < 0 || p->q_tokens > kMaxQTokens)
+    return fail(KVD_ERR_INVALID, "q_tokens must be in [0, %d] (got %d)", kMaxQTokens, p->q_tokens);
   if (elem_bits(p->kv_dtype) == 0) return fail(KVD_ERR_INVALID, "unknown kv_dtype %d", p->kv_dtype);
   if (!(p->sm_scale >= 0.0f) || !std::isfinite(p->sm_scale))
     return fail(KVD_ERR_INVALID, "sm_scale must be finite and >= 0");
@@ -89,8 +95,13 @@ int check_problem(const kvd_problem* p) {
   const double cache_bytes = (double)p->B * p->Hkv * rows *
                              (double)(p->Dqk > p->Dv ? p->Dqk : p->Dv) * elem_bits(p->kv_dtype) / 8;
   if (cache_bytes > 9.0e18) return fail(KVD_ERR_INVALID, "cache too large to index");
-  const double part_elems = (double)p->kvp * p->B * p->Hq * (double)p->Dv;
-  if (part_elems > 2.0e9) return fail(KVD_ERR_UNSUPPORTED, "kvp*B*Hq*Dv too large");
+  const double part_elems = (double)p->kvp * p->B * tokens(p) * p->Hq * (double)p->Dv;
+  if (part_elems > 2.0e9) return fail(KVD_ERR_UNSUPPORTED, "kvp*B*q_tokens*Hq*Dv too large");
+  // workgroup ids (at most one per shard, request, query token and query
+  // head, plus 8 units of padding per token) and append ids fit in int32
+  if (((double)p->kvp * p->B * p->Hq + 8.0) * tokens(p) > 2.0e9 ||
+      (double)p->B * tokens(p) * p->Hkv * 2.0 > 2.0e9)
+    return fail(KVD_ERR_UNSUPPORTED, "kvp*B*Hq*q_tokens too large");
   return KVD_OK;
 }
 
@@ -153,6 +164,7 @@ kvd::PartialArgs make_args(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv
   a.Dqk = p->Dqk;
   a.Dv = p->Dv;
   a.kvp = p->kvp;
+  a.T = (int32_t)tokens(p);
   a.S_max = p->S_max;
   set_paging(p, &a);
   a.q_bf16 = p->q_dtype == KVD_BF16;
@@ -220,11 +232,11 @@ int check_merge(int32_t kvp, int64_t rows, int32_t Dv, const float* o_part, cons
 }
 
 size_t workspace_o_bytes(const kvd_problem* p) {
-  return round_up((size_t)p->kvp * p->B * p->Hq * p->Dv * sizeof(float), kWorkspaceAlign);
+  return round_up((size_t)p->kvp * p->B * tokens(p) * p->Hq * p->Dv * sizeof(float), kWorkspaceAlign);
 }
 
 size_t workspace_lse_bytes(const kvd_problem* p) {
-  return round_up((size_t)p->kvp * p->B * p->Hq * sizeof(float), kWorkspaceAlign);
+  return round_up((size_t)p->kvp * p->B * tokens(p) * p->Hq * sizeof(float), kWorkspaceAlign);
 }
 
 }  // namespace
@@ -299,6 +311,7 @@ int kvd_append_kv(const kvd_problem* p, const float* k_new, const float* v_new,
   a.Dqk = p->Dqk;
   a.Dv = p->Dv;
   a.kvp = p->kvp;
+  a.T = (int32_t)tokens(p);
   a.S_max = p->S_max;
   a.kv_format = p->kv_dtype;
   a.v_aliases_k = p->v_aliases_k != 0;
@@ -324,7 +337,7 @@ int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v, const in
     return fail(KVD_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
   float* o_part = static_cast<float*>(workspace);
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + workspace_o_bytes(p));
-  const int64_t rows = (int64_t)p->B * p->Hq;
+  const int64_t rows = (int64_t)p->B * tokens(p) * p->Hq;
   s = check_merge(p->kvp, rows, p->Dv, o_part, lse_part, o, lse);
   if (s != KVD_OK) return s;
   // validate the kernel choice before enqueueing anything

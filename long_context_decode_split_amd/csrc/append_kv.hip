@@ -1,7 +1,8 @@
-// Append one new token per request to the cache: encode its fp32 K and V rows
-// into the cache format and store them where the cache layout puts global
-// position positions[b] (the decode step's KV write; with the striped and
-// staggered layouts every shard takes its share of the new tokens).
+// Append T new tokens per request to the cache: encode their fp32 K and V
+// rows into the cache format and store token t where the cache layout puts
+// global position positions[b] + t (the decode step's KV write, or the new
+// tokens of a multi-token turn; with the striped and staggered layouts every
+// shard takes its share of the new tokens).
 //
 // Encodings (the cache-format readings shared with the decode kernels):
 //  - bf16: round to nearest, ties to even;
@@ -12,7 +13,7 @@
 //    amax) - 2 + 127, 0, 254) (127 for an all-zero block), elements
 //    x * 2^(127 - E) rounded to nearest E2M1, ties to even, saturating at
 //    +-6; element 2i in the low nibble of byte i.
-// One workgroup of one wave per (request, KV head, K or V row); the kernel is
+// One workgroup of one wave per (request, token, KV head, K or V row); the kernel is
 // latency-bound (a few KB per call), so it favours plain code.
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
@@ -67,11 +68,14 @@ __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs a) {
   const int which = flat % rows_per_head;   // 0: K row, 1: V row
   flat /= rows_per_head;
   const int kvh = flat % a.Hkv;
-  const int b = flat / a.Hkv;
+  flat /= a.Hkv;
+  const int tok = flat % a.T;
+  const int b = flat / a.T;
   const int t = threadIdx.x;
 
-  const int64_t pos = a.positions[b];
-  if (pos < 0) return;
+  const int64_t start = a.positions[b];
+  if (start < 0) return;                           // the whole request is skipped
+  const int64_t pos = start + tok;
   const int64_t bh = (int64_t)b * a.Hkv + kvh;
   int64_t row;
   if (a.layout == kPaged) {
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs a) {
     row = slab * a.S_max + r;
   }
   const int D = which ? a.Dv : a.Dqk;
-  const float* x = (which ? a.v_new : a.k_new) + bh * D;
+  const float* x = (which ? a.v_new : a.k_new) + (((int64_t)b * a.T + tok) * a.Hkv + kvh) * D;
   uint8_t* data = static_cast<uint8_t*>(which ? a.v : a.k);
   void* scale = which ? a.v_scale : a.k_scale;
 
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs a) {
 }  // namespace
 
 hipError_t launch_append_kv(const AppendArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.B * a.Hkv * (a.v_aliases_k ? 1 : 2);
+  const int64_t blocks = (int64_t)a.B * a.T * a.Hkv * (a.v_aliases_k ? 1 : 2);
   hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }

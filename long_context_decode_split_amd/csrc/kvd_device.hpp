@@ -195,37 +195,47 @@ __device__ __forceinline__ void shard_range(int64_t L, int kvp, int j, int64_t* 
 // Cache layouts (kvd_layout of kvd.h).
 enum CacheLayout : int { kContiguous = 0, kStriped = 1, kStaggered16 = 2, kPaged = 3 };
 
-// What shard j of request b reads for KV head kvh: the slab (index of its
-// [S_max, row] block in the cache tensor) and its token rows [s0, s1).
+// What shard j of request b reads for KV head kvh on behalf of query token t
+// of T: the slab (index of its [S_max, row] block in the cache tensor) and
+// its token rows [s0, s1).
 //  contiguous: cache [B,Hkv,S_max,.]; the split rule cuts [0, L).
 //  striped / staggered16: cache [kvp,B,Hkv,S_max,.]; shard j holds its L_j
 //  tokens at rows [0, L_j), L_j the number of positions i < L it owns
 //  (i mod kvp == j, resp. (i div 16) mod kvp == j).
+// Causal cut: query token t of a T-token turn sits at position L - T + t and
+// sees positions below vis = L - T + 1 + t.  The positions a shard holds grow
+// with its row, so what t sees of a shard is a prefix of its rows: the split
+// rule's range cut at vis (contiguous, paged), or the owner count of the
+// first vis positions (striped, staggered).  T = 1 sees the whole shard.
 // Lengths are clamped so that no row outside the slab is ever read.
 struct ShardSpan {
   int64_t slab, s0, s1;
 };
 
-__device__ __forceinline__ ShardSpan shard_span(int layout, int64_t L, int64_t S_max, int kvp,
+__device__ __forceinline__ ShardSpan shard_span(int layout, int64_t L, int T, int t, int64_t S_max, int kvp,
                                                 int B, int Hkv, int j, int b, int kvh) {
   ShardSpan sp;
   if (layout == kContiguous || layout == kPaged) {
     // (paged: S_max is the request capacity max_blocks * block_len; rows are
     // found through the block table, see phys_row)
     L = L < 0 ? 0 : (L > S_max ? S_max : L);
+    const int64_t vis = L - (T - 1 - t);
     sp.slab = (int64_t)b * Hkv + kvh;
     shard_range(L, kvp, j, &sp.s0, &sp.s1);
+    if (vis < sp.s1) sp.s1 = vis > sp.s0 ? vis : sp.s0;
     return sp;
   }
   const int64_t cap = S_max * kvp;
   L = L < 0 ? 0 : (L > cap ? cap : L);
+  int64_t vis = L - (T - 1 - t);
+  vis = vis < 0 ? 0 : vis;
   int64_t Lj;
   if (layout == kStriped) {
-    Lj = L > j ? (L - 1 - j) / kvp + 1 : 0;
+    Lj = vis > j ? (vis - 1 - j) / kvp + 1 : 0;
   } else {
     const int64_t run = 16 * (int64_t)kvp;
-    const int64_t full = L / run;
-    int64_t rem = L - full * run - 16 * (int64_t)j;
+    const int64_t full = vis / run;
+    int64_t rem = vis - full * run - 16 * (int64_t)j;
     rem = rem < 0 ? 0 : (rem > 16 ? 16 : rem);
     Lj = 16 * full + rem;
   }
@@ -233,6 +243,27 @@ __device__ __forceinline__ ShardSpan shard_span(int layout, int64_t L, int64_t S
   sp.s0 = 0;
   sp.s1 = Lj < S_max ? Lj : S_max;
   return sp;
+}
+
+// Workgroup id -> (work unit u, query token t) for a pass of U units with T
+// query tokens each (see unit_token_blocks in kvd_internal.hpp for the grid).
+// The T workgroups of one unit read the same cache rows.  Workgroups go to the
+// 8 XCDs round-robin by id, so ids are laid out in groups of 8 units x T
+// tokens, unit u and token t at id (u div 8) 8T + 8t + u mod 8: every token
+// of a unit runs on the same XCD, where the rows one of them brings into that
+// XCD's L2 serve the others, and they are dispatched back to back.  Returns
+// false for the padding ids of a last, partial group of units.
+__device__ __forceinline__ bool unit_token(int64_t id, int64_t U, int T, int64_t* u, int* t) {
+  if (T == 1) {
+    *u = id;
+    *t = 0;
+    return true;
+  }
+  const int64_t grp = id / (8 * (int64_t)T);
+  const int r = (int)(id - grp * 8 * (int64_t)T);
+  *t = r >> 3;
+  *u = grp * 8 + (r & 7);
+  return *u < U;
 }
 
 // Physical row (index into the cache tensor viewed as rows) of token t of

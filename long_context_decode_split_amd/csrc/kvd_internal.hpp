@@ -17,6 +17,7 @@ struct PartialArgs {
   float* o_part;
   float* lse_part;
   int32_t B, Hq, Hkv, Dqk, Dv, kvp;
+  int32_t T;              // query tokens per request (q [B,T,Hq,Dqk])
   int64_t S_max;
   int32_t q_bf16;         // q is bf16 (else fp32)
   int32_t kv_format;      // KvFormat
@@ -32,14 +33,15 @@ struct PartialArgs {
 
 // Arguments of one append (kvd_append_kv), already validated by api.cpp.
 struct AppendArgs {
-  const float* k_new;     // [B,Hkv,Dqk]
-  const float* v_new;     // [B,Hkv,Dv]; nullptr when V aliases K
-  const int32_t* positions;
+  const float* k_new;     // [B,T,Hkv,Dqk]
+  const float* v_new;     // [B,T,Hkv,Dv]; nullptr when V aliases K
+  const int32_t* positions;   // [B]: token t of request b goes to positions[b] + t
   void* k;
   void* k_scale;
   void* v;
   void* v_scale;
   int32_t B, Hkv, Dqk, Dv, kvp;
+  int32_t T;              // new tokens per request
   int64_t S_max;
   int32_t kv_format;
   int32_t v_aliases_k;
@@ -49,6 +51,11 @@ struct AppendArgs {
   int32_t max_blocks;
   int64_t num_blocks;
 };
+
+// Grid of a partial pass of U work units with T query tokens each (the id
+// layout is unit_token's in kvd_device.hpp): U for T = 1, else U rounded up
+// to a multiple of 8 units, times T.
+inline int64_t unit_token_blocks(int64_t U, int T) { return T == 1 ? U : (U + 7) / 8 * 8 * T; }
 
 // Each family reports whether it handles a problem, then launches it.
 bool valu_supports(const PartialArgs& a);

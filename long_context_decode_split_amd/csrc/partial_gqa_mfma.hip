@@ -17,7 +17,8 @@
 // pair hi + lo (two MFMAs), which keeps ~16 significant bits instead of 8, so
 // the output error stays near fp32 level even for short shards.
 //
-// Work split: one workgroup of 4 waves per (shard j, request b, KV head); wave
+// Work split: one workgroup of 4 waves per (shard j, request b, KV head,
+// query token t; a single-token decode has t = 0 only); wave
 // w takes the shard's 32-token tiles w, w+4, w+8, ... and keeps the loads of
 // its next one (bf16) or two (fp8, MXFP4: smaller tiles) tiles in flight while
 // computing the current one, so enough bytes are outstanding to cover HBM
@@ -126,13 +127,17 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
-  int flat = blockIdx.x;
-  const int kvh = flat % a.Hkv;
-  flat /= a.Hkv;
-  const int b = flat % a.B;
-  const int j = flat / a.B;
+  // unit (shard j, request b, KV head kvh) and query token qt
+  int64_t unit;
+  int qt;
+  if (!unit_token(blockIdx.x, (int64_t)a.kvp * a.B * a.Hkv, a.T, &unit, &qt)) return;
+  const int kvh = (int)(unit % a.Hkv);
+  const int b = (int)(unit / a.Hkv % a.B);
+  const int j = (int)(unit / ((int64_t)a.Hkv * a.B));
+  const int64_t qrow0 = ((int64_t)b * a.T + qt) * a.Hq + kvh * 16;                // q row of head n: qrow0 + n
+  const int64_t orow0 = (((int64_t)j * a.B + b) * a.T + qt) * a.Hq + kvh * 16;    // o_part / lse_part row
 
-  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
+  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.T, qt, a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
   const int64_t s0 = span.s0, s1 = span.s1;
   const int64_t slab = span.slab;                  // cache block of this shard
   const int64_t bh = (int64_t)b * a.Hkv + kvh;     // fp8 scales are per (request, KV head)
@@ -168,8 +173,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   // Q^T operand: lane (n, g) holds head n, the 8 d of chunk c for group g.
   bf16x8_t qop[4];
   {
-    const int h = kvh * 16 + r16;
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h) * kD;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (qrow0 + r16) * kD;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint4 v = *reinterpret_cast<const uint4*>(qrow + Lay::chunk_d(c, g));
@@ -492,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       }
       o = ot / lt * vscale;
     }
-    a.o_part[(((int64_t)j * a.B + b) * a.Hq + kvh * 16 + n) * kD + d] = o;
+    a.o_part[(orow0 + n) * kD + d] = o;
   }
   if (tid < 16) {
     float M = sh_m[0][tid];
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       for (int w = 0; w < kWaves; ++w) lt += sh_l[w][tid] * rescale_weight(sh_m[w][tid], M);
       lse = (M + fast_log2(lt)) * kLn2;
     }
-    a.lse_part[((int64_t)j * a.B + b) * a.Hq + kvh * 16 + tid] = lse;
+    a.lse_part[orow0 + tid] = lse;
   }
 }
 
@@ -527,7 +531,7 @@ void launch_gqa(const PartialArgs& a, int64_t blocks, hipStream_t stream) {
 }
 
 hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.kvp * a.B * a.Hkv;
+  const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, a.T);
   switch (a.kv_format) {
     case kBF16: launch_gqa<kBF16, false>(a, blocks, stream); break;
     case kFP8: launch_gqa<kFP8, false>(a, blocks, stream); break;

@@ -12,7 +12,8 @@
 // accumulator (256 AGPRs per wave) is never rescaled: see the pass structure
 // below.
 //
-// Work split: one workgroup of 4 waves per (shard j, request b, KV head).  The
+// Work split: one workgroup of 4 waves per (shard j, request b, KV head, query
+// token; a single-token decode has one).  The
 // shard is walked in 32-token tiles shared by all four waves; wave w owns heads
 // 32w .. 32w+31, keeping their Q (144 VGPRs) and their O^T accumulator (32 heads
 // x 512 dv, 256 AGPRs) in registers for the whole shard; LDS traffic per
@@ -119,13 +120,17 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
-  int flat = blockIdx.x;
-  const int kvh = flat % a.Hkv;
-  flat /= a.Hkv;
-  const int b = flat % a.B;
-  const int j = flat / a.B;
+  // unit (shard j, request b, KV head kvh) and query token qt
+  int64_t unit;
+  int qt;
+  if (!unit_token(blockIdx.x, (int64_t)a.kvp * a.B * a.Hkv, a.T, &unit, &qt)) return;
+  const int kvh = (int)(unit % a.Hkv);
+  const int b = (int)(unit / a.Hkv % a.B);
+  const int j = (int)(unit / ((int64_t)a.Hkv * a.B));
+  const int64_t qrow0 = ((int64_t)b * a.T + qt) * a.Hq;                // q row of head h: qrow0 + h
+  const int64_t orow0 = (((int64_t)j * a.B + b) * a.T + qt) * a.Hq;    // o_part / lse_part row
 
-  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
+  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.T, qt, a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
   const int64_t s0 = span.s0, s1 = span.s1;
   const int64_t slab = span.slab;                  // cache block of this shard
   const int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + head0 + 16 * hb + r16) * kDqk;
+        static_cast<const uint16_t*>(a.q) + (qrow0 + head0 + 16 * hb + r16) * kDqk;
 #pragma unroll
     for (int c = 0; c < 18; ++c) {
       const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g);
@@ -399,14 +404,14 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
     const bool empty = (m2[hb] == -INFINITY);
     const float inv = empty ? 0.0f : 1.0f / lt;
     const int h = head0 + 16 * hb + r16;
-    float* orow = a.o_part + (((int64_t)j * a.B + b) * a.Hq + h) * kDv;
+    float* orow = a.o_part + (orow0 + h) * kDv;
 #pragma unroll
     for (int blk = 0; blk < 32; ++blk) {
       const f32x4_t v = acc[hb][blk] * inv;
       *reinterpret_cast<float4*>(orow + 16 * blk + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
     }
     if (g == 0)
-      a.lse_part[((int64_t)j * a.B + b) * a.Hq + h] = empty ? -INFINITY : (m2[hb] + fast_log2(lt)) * kLn2;
+      a.lse_part[orow0 + h] = empty ? -INFINITY : (m2[hb] + fast_log2(lt)) * kLn2;
   }
 }
 
@@ -433,7 +438,7 @@ hipError_t launch_partial_mla_mfma(const PartialArgs& a, hipStream_t stream) {
     }
     configured = true;
   }
-  const int64_t blocks = (int64_t)a.kvp * a.B * a.Hkv;
+  const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, a.T);
   if (a.layout == kPaged)
     hipLaunchKernelGGL(mla_mfma_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), kSmemBytes, stream, a);
   else

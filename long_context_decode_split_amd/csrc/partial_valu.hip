@@ -2,7 +2,7 @@
 //
 // Handles every KV format for head widths 64, 128 and 256 (MXFP4: 128, 256)
 // and any query-head group size G.  One workgroup (4 waves) owns one
-// (shard j, request b, KV head, chunk of up to HC query heads).  Each wave is
+// (shard j, request b, KV head, chunk of up to HC query heads, query token).  Each wave is
 // four DPP rows of 16 lanes; a row owns one cached token at a time and each
 // lane holds D/16 consecutive elements of that token's K and V rows, so a row
 // streams whole cache rows with coalesced 4-64 byte loads.  The 16 rows of the
@@ -41,14 +41,19 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
 
   const int G = a.Hq / a.Hkv;
   const int nhc = (G + HC - 1) / HC;
-  int flat = blockIdx.x;
-  const int hc = flat % nhc;
-  flat /= nhc;
-  const int kvh = flat % a.Hkv;
+  // unit (shard j, request b, KV head kvh, head chunk hc) and query token qt
+  int64_t unit;
+  int qt;
+  if (!unit_token(blockIdx.x, (int64_t)a.kvp * a.B * a.Hkv * nhc, a.T, &unit, &qt)) return;
+  const int hc = (int)(unit % nhc);
+  int64_t flat = unit / nhc;
+  const int kvh = (int)(flat % a.Hkv);
   flat /= a.Hkv;
-  const int b = flat % a.B;
-  const int j = flat / a.B;
+  const int b = (int)(flat % a.B);
+  const int j = (int)(flat / a.B);
   const int h0 = kvh * G + hc * HC;
+  const int64_t qrow0 = ((int64_t)b * a.T + qt) * a.Hq;                // q row of head h: qrow0 + h
+  const int64_t orow0 = (((int64_t)j * a.B + b) * a.T + qt) * a.Hq;    // o_part / lse_part row
   const int nh = min(HC, G - hc * HC);
 
   const int tid = threadIdx.x;
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
   const int li = lane & 15;
   const int row = wave * 4 + (lane >> 4);
 
-  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
+  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.T, qt, a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
   const int64_t s0 = span.s0, s1 = span.s1;
   const int64_t slab = span.slab;                  // cache block of this shard
   const int64_t bh = (int64_t)b * a.Hkv + kvh;     // fp8 scales are per (request, KV head)
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
 #pragma unroll
     for (int i = 0; i < HC; ++i) {
       const int h = h0 + (i < nh ? i : nh - 1);
-      const int64_t off = ((int64_t)b * a.Hq + h) * DQK + li * EK;
+      const int64_t off = (qrow0 + h) * DQK + li * EK;
       if constexpr (QBF16) {
         uint32_t w[EK / 2];
 #pragma unroll
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
       }
       o = osum / lsum * vscale;
     }
-    a.o_part[(((int64_t)j * a.B + b) * a.Hq + h0 + i) * DV + d] = o;
+    a.o_part[(orow0 + h0 + i) * DV + d] = o;
   }
   for (int i = tid; i < nh; i += kThreads) {
     float M = sh_m[0][i];
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
       for (int w = 0; w < 4; ++w) lsum += sh_l[w][i] * rescale_weight(sh_m[w][i], M);
       lse = (M + fast_log2(lsum)) * kLn2;
     }
-    a.lse_part[((int64_t)j * a.B + b) * a.Hq + h0 + i] = lse;
+    a.lse_part[orow0 + h0 + i] = lse;
   }
 }
 
@@ -281,7 +286,7 @@ hipError_t launch_partial_valu(const PartialArgs& a, hipStream_t stream) {
   if (fn == nullptr) return hipErrorInvalidValue;
   const int G = a.Hq / a.Hkv;
   const int hc = a.Dqk <= 128 ? 8 : 4;
-  const int64_t blocks = (int64_t)a.kvp * a.B * a.Hkv * ((G + hc - 1) / hc);
+  const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv * ((G + hc - 1) / hc), a.T);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

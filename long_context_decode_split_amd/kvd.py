@@ -31,7 +31,7 @@ LAYOUT_CODES = {"contiguous": KVD_LAYOUT_CONTIGUOUS, "striped": KVD_LAYOUT_STRIP
 # Every symbol include/kvd.h declares.
 EXPORTED = ("kvd_decode_partial", "kvd_lse_merge", "kvd_decode_workspace_bytes", "kvd_decode",
             "kvd_append_kv", "kvd_status_string", "kvd_last_error", "kvd_abi_version")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class KvdProblem(ctypes.Structure):
@@ -40,7 +40,7 @@ class KvdProblem(ctypes.Structure):
                 ("kvp", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("v_aliases_k", ctypes.c_int32), ("layout", ctypes.c_int32),
                 ("block_len", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("num_blocks", ctypes.c_int64),
-                ("block_table", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("q_tokens", ctypes.c_int32)]
 
 
 class KvdKV(ctypes.Structure):
@@ -94,16 +94,19 @@ def lib() -> ctypes.CDLL:
 
 
 def problem(B, Hq, Hkv, Dqk, Dv, S_max, kvp, q_dtype, kv_dtype, sm_scale=0.0, v_aliases_k=False,
-            layout="contiguous", block_len=0, max_blocks=0, num_blocks=0, block_table=None) -> KvdProblem:
+            layout="contiguous", block_len=0, max_blocks=0, num_blocks=0, block_table=None,
+            q_tokens=1) -> KvdProblem:
     """A kvd_problem; dtypes may be KVD_* codes or 'f32' / 'bf16' / 'fp8' / 'mxfp4', the layout a
     KVD_LAYOUT_* code or 'contiguous' / 'striped' / 'staggered16' / 'paged' (then block_len,
-    max_blocks, num_blocks and the device block_table [B,max_blocks] int32 describe the pool).
+    max_blocks, num_blocks and the device block_table [B,max_blocks] int32 describe the pool);
+    q_tokens is T, the query (and appended) tokens per request.
     The problem holds block_table's address: keep the tensor alive while it is used."""
     qd = DTYPE_CODES.get(q_dtype, q_dtype)
     kd = DTYPE_CODES.get(kv_dtype, kv_dtype)
     lay = LAYOUT_CODES.get(layout, layout)
     return KvdProblem(B, Hq, Hkv, Dqk, Dv, S_max, kvp, qd, kd, float(sm_scale), int(bool(v_aliases_k)),
-                      int(lay), int(block_len), int(max_blocks), int(num_blocks), _ptr(block_table))
+                      int(lay), int(block_len), int(max_blocks), int(num_blocks), _ptr(block_table),
+                      int(q_tokens))
 
 
 def _ptr(x):

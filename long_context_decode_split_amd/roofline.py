@@ -55,6 +55,17 @@ def attention_flops(Hq: int, seq_lens, Dqk: int, Dv: int) -> int:
     return 2 * Hq * tokens * (Dqk + Dv)
 
 
+def attention_flops_tokens(Hq: int, seq_lens, T: int, Dqk: int, Dv: int) -> int:
+    """Flops of T query tokens per request with causal visibility among them:
+    query t of a request with L cached tokens (the T new ones included) sees
+    max(0, L - T + 1 + t) of them."""
+    tokens = 0
+    for s in seq_lens:
+        L = int(s)
+        tokens += sum(max(0, min(L, L - T + 1 + t)) for t in range(T))
+    return 2 * Hq * tokens * (Dqk + Dv)
+
+
 def partial_bytes(kvp: int, B: int, Hq: int, Dv: int) -> int:
     """Bytes of the shard partials (o_part fp32 + lse_part fp32)."""
     return kvp * B * Hq * (Dv + 1) * 4

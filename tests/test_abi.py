@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvd.kvd_abi_version() == kvd.ABI_VERSION == 3
+    assert kvd.kvd_abi_version() == kvd.ABI_VERSION == 4
     for s in range(4):
         assert kvd.kvd_status_string(s).startswith(("KVD_OK", "KVD_ERR"))
     assert "unknown" in kvd.kvd_status_string(99)
@@ -75,6 +75,8 @@ def call_decode(p, ws=FAKE, o=FAKE, lse=FAKE, k=(FAKE, FAKE), v=(FAKE, FAKE)):
     (dict(sm_scale=-1.0), INV), (dict(sm_scale=float("inf")), INV), (dict(sm_scale=float("nan")), INV),
     (dict(kv_dtype="mxfp4", Dqk=48, Dv=48), INV),
     (dict(layout=3), INV), (dict(layout=-1), INV),
+    (dict(q_tokens=-1), INV), (dict(q_tokens=65537), INV),
+    (dict(q_tokens=65536, kvp=4096, B=64), UNS),         # too many workgroups
     (dict(Dqk=96, Dv=96), UNS),             # well formed, no kernel for this width
     (dict(Dqk=128, Dv=64), UNS),
 ])
@@ -130,6 +132,10 @@ def test_workspace_bytes():
     lse_bytes = 8 * 2 * 32 * 4
     assert n == -(-o_bytes // 256) * 256 + -(-lse_bytes // 256) * 256
     assert kvd.kvd_decode_workspace_bytes(good_problem(B=0)) == 0
+    # T query tokens: T times the rows; q_tokens = 0 means one token
+    assert kvd.kvd_decode_workspace_bytes(good_problem(kvp=8, q_tokens=0)) == n
+    t5 = kvd.kvd_decode_workspace_bytes(good_problem(kvp=8, q_tokens=5))
+    assert t5 == -(-5 * o_bytes // 256) * 256 + -(-5 * lse_bytes // 256) * 256
 
 
 def test_decode_validation_happens_before_launch():
@@ -182,3 +188,20 @@ def test_paged_problem_validation(kw):
     assert call_partial(good_problem(**base)) == INV
     assert call_append(good_problem(**base)) == INV
     assert kvd.kvd_decode_workspace_bytes(good_problem(**base)) == 0
+
+
+def test_problem_struct_matches_header(tmp_path):
+    """The binding's kvd_problem has the C struct's size and field offsets
+    (compiled against include/kvd.h with the host compiler)."""
+    fields = [f[0] for f in kvd.KvdProblem._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "kvd.h"\nint main(void) {\n'
+                   '  printf("size %zu\\n", sizeof(kvd_problem));\n' +
+                   "".join('  printf("%s %%zu\\n", offsetof(kvd_problem, %s));\n' % (f, f) for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
+    got = dict(line.split() for line in subprocess.check_output([str(exe)], text=True).splitlines())
+    assert int(got["size"]) == ctypes.sizeof(kvd.KvdProblem)
+    for f in fields:
+        assert int(got[f]) == getattr(kvd.KvdProblem, f).offset, f

@@ -54,3 +54,10 @@ def test_row_bytes():
     assert roofline.row_bytes("fp8", 128) == 128
     assert roofline.kv_bytes(8, [1 << 20] * 8, 128, 128, "fp8", False) == 17179869184 + 8 * 8 * 8
     assert roofline.kv_bytes(1, [1 << 19] * 8, 576, 512, "bf16", True) == 4831838208
+
+
+def test_multi_token_flops_count_each_visible_pair():
+    # T = 3 queries over L = 5 tokens see 3, 4, 5 tokens; L = 1 sees 0, 0, 1
+    fl = roofline.attention_flops_tokens(2, [5, 1], 3, 8, 4)
+    assert fl == 2 * 2 * (3 + 4 + 5 + 0 + 0 + 1) * (8 + 4)
+    assert roofline.attention_flops_tokens(7, [9, 4], 1, 16, 16) == roofline.attention_flops(7, [9, 4], 16, 16)
