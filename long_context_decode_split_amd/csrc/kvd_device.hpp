@@ -47,18 +47,28 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // Streaming (non-temporal) loads of cache bytes.  Every cached byte is read
 // once per call, so the loads carry the non-temporal hint; on MI355X this is
 // what lets a read stream approach HBM peak (regular loads plateau ~10%
-// lower).  p must be aligned to the access size.
+// lower).  NT = false gives plain loads, for bytes that several workgroups
+// read (the query tokens of a multi-token turn), which the caches should
+// keep.  p must be aligned to the access size.
+template <bool NT = true>
 __device__ __forceinline__ u32x4_t stream_load16(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  else return *reinterpret_cast<const u32x4_t*>(p);
 }
+template <bool NT = true>
 __device__ __forceinline__ u32x2_t stream_load8(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  else return *reinterpret_cast<const u32x2_t*>(p);
 }
+template <bool NT = true>
 __device__ __forceinline__ uint32_t stream_load4(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  else return *reinterpret_cast<const uint32_t*>(p);
 }
+template <bool NT = true>
 __device__ __forceinline__ uint32_t stream_load1(const uint8_t* p) {
-  return __builtin_nontemporal_load(p);
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
 }
 
 // Load N bytes (N in {4, 8, 16, 32, 64}) from a 4-byte-aligned (N >= 16:

@@ -110,12 +110,94 @@ struct Raw {
   uint32_t vs[8];                              // MXFP4: the 4 V block exponents of each token
 };
 
+// K operand of MFMA chunk c of half-tile u (the 8 dims Layout::chunk_d(c, g)
+// of token 16u + r16), decoded to bf16.
+template <int KV>
+__device__ __forceinline__ bf16x8_t k_operand(const Raw<KV>& rw, int u, int c) {
+  if constexpr (KV == kBF16) {
+    return as_bf16x8(rw.k[u][4 * c], rw.k[u][4 * c + 1], rw.k[u][4 * c + 2], rw.k[u][4 * c + 3]);
+  } else if constexpr (KV == kFP8) {
+    const uint32_t w0 = rw.k[u][2 * c], w1 = rw.k[u][2 * c + 1];
+    return __builtin_bit_cast(
+        bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))});
+  } else {
+    const float ksc = e8m0_to_f32_fast(rw.ks[u]);
+    const uint32_t w = rw.k[u][c];
+    return __builtin_bit_cast(
+        bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 0)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 1)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 2)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 3))});
+  }
+}
+
+// V^T operands of the 8 16-column blocks of the PV product, decoded to bf16:
+// f(blk, op) is called for each block as soon as its operand is ready.  The
+// operand of block blk holds the lane's column of that block for the 8 tokens
+// {4g + i, 16 + 4g + i}, in the k order of the P^T operand.
+template <int KV, class F>
+__device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_shift, F&& f) {
+  if constexpr (KV == kBF16 || KV == kMXFP4) {
+    // token-major bf16 pairs cv[e][q] = columns (8 r16 + 2q, 8 r16 + 2q + 1) of token e
+    uint32_t cv[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (KV == kBF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cv[e][q] = rw.v[e][q];
+      } else {
+        const float vsc = e8m0_to_f32_fast(__builtin_amdgcn_ubfe(rw.vs[e], vs_shift, 8));
+        const uint32_t w = rw.v[e][0];
+        cv[e][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 0));
+        cv[e][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 1));
+        cv[e][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 2));
+        cv[e][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 3));
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      const int q = blk / 2;
+      const uint32_t sel = (blk & 1) ? 0x07060302u : 0x05040100u;
+      f(blk, as_bf16x8(perm(cv[1][q], cv[0][q], sel), perm(cv[3][q], cv[2][q], sel),
+                       perm(cv[5][q], cv[4][q], sel), perm(cv[7][q], cv[6][q], sel)));
+    }
+  } else {
+    // fp8: interleave bytes of token pairs, then convert both halves
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; s2 += 2) {
+        const uint32_t sel = (s2 == 0) ? 0x05010400u : 0x07030602u;
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint32_t x2 = perm(rw.v[2 * rr + 1][q], rw.v[2 * rr][q], sel);
+          lo[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, false));
+          hi[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, true));
+        }
+        f(4 * q + s2, as_bf16x8(lo[0], lo[1], lo[2], lo[3]));
+        f(4 * q + s2 + 1, as_bf16x8(hi[0], hi[1], hi[2], hi[3]));
+      }
+    }
+  }
+}
+
 // VS16 (MXFP4 only): every 16-token run of V scale rows is 16-byte aligned.
 // PAGED: rows are found through the block table (paged cache layout).
-template <int KV, bool VS16, bool PAGED>
+// NT: cache loads carry the non-temporal hint (one query token: every byte is
+// read once); several query tokens read each byte once per token chunk, from
+// the caches when the loads are plain.
+// TW: query tokens per workgroup.  Each wave decodes a tile once and runs the
+// logits, softmax and PV product of each of the TW tokens on it; every token
+// keeps its own Q operands, softmax state and accumulator.
+template <int KV, bool VS16, bool PAGED, bool NT, int TW>
 __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   using Lay = Layout<KV>;
   constexpr int64_t ROW = Lay::kRowBytes;
+  constexpr int kRing = TW > 1 ? 2 : Lay::kRing;
 
   __shared__ float sh_o[kWaves][16][kD + 4];
   __shared__ float sh_m[kWaves][16];
@@ -127,18 +209,28 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
-  // unit (shard j, request b, KV head kvh) and query token qt
+  // unit (shard j, request b, KV head kvh) and chunk of TW query tokens
+  const int nchunks = (a.T + TW - 1) / TW;
   int64_t unit;
-  int qt;
-  if (!unit_token(blockIdx.x, (int64_t)a.kvp * a.B * a.Hkv, a.T, &unit, &qt)) return;
+  int chunk;
+  if (!unit_token(blockIdx.x, (int64_t)a.kvp * a.B * a.Hkv, nchunks, &unit, &chunk)) return;
   const int kvh = (int)(unit % a.Hkv);
   const int b = (int)(unit / a.Hkv % a.B);
   const int j = (int)(unit / ((int64_t)a.Hkv * a.B));
-  const int64_t qrow0 = ((int64_t)b * a.T + qt) * a.Hq + kvh * 16;                // q row of head n: qrow0 + n
-  const int64_t orow0 = (((int64_t)j * a.B + b) * a.T + qt) * a.Hq + kvh * 16;    // o_part / lse_part row
+  const int qt0 = chunk * TW;                       // first query token of the chunk
+  const int nq = a.T - qt0 < TW ? a.T - qt0 : TW;   // tokens of the chunk that exist
 
-  const ShardSpan span = shard_span(a.layout, a.seq_lens[b], a.T, qt, a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
+  // The rows the shard holds are [s0, s1); token i of the chunk sees rows
+  // [s0, s1t[i]) (its causal cut).  Later tokens see more, so the last one
+  // bounds the rows read; tokens past the end of T see none.
+  const int64_t L = a.seq_lens[b];
+  const ShardSpan span = shard_span(a.layout, L, a.T, qt0 + nq - 1, a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
   const int64_t s0 = span.s0, s1 = span.s1;
+  int64_t s1t[TW];
+#pragma unroll
+  for (int i = 0; i < TW; ++i)
+    s1t[i] = i >= nq ? s0 : (i == nq - 1 ? s1 : shard_span(a.layout, L, a.T, qt0 + i, a.S_max, a.kvp, a.B, a.Hkv,
+                                                            j, b, kvh).s1);
   const int64_t slab = span.slab;                  // cache block of this shard
   const int64_t bh = (int64_t)b * a.Hkv + kvh;     // fp8 scales are per (request, KV head)
   const int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
@@ -170,22 +262,30 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   }
   const float c2 = a.scale_log2 * kscale;  // raw logit -> log2 domain
 
-  // Q^T operand: lane (n, g) holds head n, the 8 d of chunk c for group g.
-  bf16x8_t qop[4];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (qrow0 + r16) * kD;
+  // Q^T operands: lane (n, g) holds head n, the 8 d of chunk c for group g,
+  // of each token of the chunk (a token past the end of T loads the last one's).
+  bf16x8_t qop[TW][4];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    const int qt = qt0 + (i < nq ? i : nq - 1);
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.T + qt) * a.Hq + kvh * 16 + r16) * kD;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint4 v = *reinterpret_cast<const uint4*>(qrow + Lay::chunk_d(c, g));
-      qop[c] = as_bf16x8(v.x, v.y, v.z, v.w);
+      qop[i][c] = as_bf16x8(v.x, v.y, v.z, v.w);
     }
   }
 
-  f32x4_t acc[8];
+  f32x4_t acc[TW][8];
+  float m2[TW];    // running max of this lane's head (log2 domain)
+  float lsum[TW];  // partial sum of P over this lane's tokens
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m2 = -INFINITY;  // running max of this lane's head (log2 domain)
-  float lsum = 0.0f;     // partial sum of P over this lane's tokens
+  for (int i = 0; i < TW; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[i][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m2[i] = -INFINITY;
+    lsum[i] = 0.0f;
+  }
 
   const int64_t last = s1 - 1;
   // Per-lane byte offsets inside a tile (loop invariant, 32-bit): a full tile
@@ -226,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < Lay::kKLoads; ++i) {
-        const u32x4_t v = stream_load16(p + 64 * i);
+        const u32x4_t v = stream_load16<NT>(p + 64 * i);
         rw.k[u][4 * i + 0] = v[0];
         rw.k[u][4 * i + 1] = v[1];
         rw.k[u][4 * i + 2] = v[2];
@@ -234,9 +334,9 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       }
       if constexpr (KV == kMXFP4) {
         if constexpr (FULL) {
-          rw.ks[u] = stream_load1(ksdata + hr[u] * SROW + ksoff);
+          rw.ks[u] = stream_load1<NT>(ksdata + hr[u] * SROW + ksoff);
         } else {
-          rw.ks[u] = stream_load1(ksdata + pt * SROW + g);
+          rw.ks[u] = stream_load1<NT>(ksdata + pt * SROW + g);
         }
       }
     }
@@ -244,18 +344,18 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if constexpr (FULL && VS16) {
-          const u32x4_t v = stream_load16(vsdata + hr[u] * SROW + vsoff);
+          const u32x4_t v = stream_load16<NT>(vsdata + hr[u] * SROW + vsoff);
 #pragma unroll
           for (int i = 0; i < 4; ++i) rw.vs[4 * u + i] = v[i];
         } else if constexpr (FULL) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rw.vs[4 * u + i] = stream_load4(vsdata + hr[u] * SROW + vsoff + 4 * i);
+          for (int i = 0; i < 4; ++i) rw.vs[4 * u + i] = stream_load4<NT>(vsdata + hr[u] * SROW + vsoff + 4 * i);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             int64_t t = base + 16 * u + 4 * g + i;
             t = t < last ? t : last;
-            rw.vs[4 * u + i] = stream_load4(vsdata + hrow(t) * SROW);
+            rw.vs[4 * u + i] = stream_load4<NT>(vsdata + hrow(t) * SROW);
           }
         }
       }
@@ -271,90 +371,64 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
         p = vdata + hrow(t) * ROW + Lay::kVBytes * r16;
       }
       if constexpr (Lay::kVBytes == 16) {
-        const u32x4_t v = stream_load16(p);
+        const u32x4_t v = stream_load16<NT>(p);
         rw.v[e][0] = v[0];
         rw.v[e][1] = v[1];
         rw.v[e][2] = v[2];
         rw.v[e][3] = v[3];
       } else if constexpr (Lay::kVBytes == 8) {
-        const u32x2_t v = stream_load8(p);
+        const u32x2_t v = stream_load8<NT>(p);
         rw.v[e][0] = v[0];
         rw.v[e][1] = v[1];
       } else {
-        rw.v[e][0] = stream_load4(p);
+        rw.v[e][0] = stream_load4<NT>(p);
       }
     }
   };
 
-  // MASK: the tile runs past the shard end; its extra tokens get zero weight.
-  auto compute = [&](const Raw<KV>& rw, int tile, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int64_t base = s0 + (int64_t)tile * kTile;
-    // ---- logits S^T = K Q^T for the two half-tiles
-    f32x4_t s[2];
+  // Logits S^T = K Q^T of one query token for the two half-tiles, as 8
+  // values per lane: head n = r16, tokens base + 16u + 4g + i at x[4u + i].
+  auto logits = [&](const Raw<KV>& rw, bf16x8_t (&kop)[2][4], const bf16x8_t (&q)[4], float (&x)[8]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      s[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      float ksc = 1.0f;
-      if constexpr (KV == kMXFP4) ksc = e8m0_to_f32_fast(rw.ks[u]);
+      f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        bf16x8_t kop;
-        if constexpr (KV == kBF16) {
-          kop = as_bf16x8(rw.k[u][4 * c], rw.k[u][4 * c + 1], rw.k[u][4 * c + 2], rw.k[u][4 * c + 3]);
-        } else if constexpr (KV == kFP8) {
-          const uint32_t w0 = rw.k[u][2 * c], w1 = rw.k[u][2 * c + 1];
-          kop = __builtin_bit_cast(
-              bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))});
-        } else {
-          const uint32_t w = rw.k[u][c];
-          kop = __builtin_bit_cast(
-              bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 0)),
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 1)),
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 2)),
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 3))});
-        }
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[c], s[u], 0, 0, 0);
+        if constexpr (TW == 1) kop[u][c] = k_operand<KV>(rw, u, c);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u][c], q[c], s, 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * u + i] = s[i];
     }
-    // ---- online softmax for head n = r16 over tokens base + 16u + 4g + i
-    float x[8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * u + i] = s[u][i];
-    if constexpr (MASK) {
-      const int nvalid = (int)(s1 - base);
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * u + 4 * g + i >= nvalid) x[4 * u + i] = -INFINITY;
-    }
+  };
+  // Tile max of the lane's head in the log2 domain.
+  auto tile_max2 = [&](const float (&x)[8]) {
     float tmax = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-    const float tmax2 = rows4_max(tmax) * c2;
-    if (__any(tmax2 > m2 + kLazyMax)) {
-      const float mn = fmaxf(m2, tmax2);
-      const float al = fast_exp2(m2 - mn);
-      lsum *= al;
+    return rows4_max(tmax) * c2;
+  };
+  // Move the running max to mn, rescaling the state.
+  auto rescale = [&](float& m, float& l, f32x4_t (&o)[8], float mn) {
+    const float al = fast_exp2(m - mn);
+    l *= al;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= al;
-      m2 = mn;
-    }
+    for (int i = 0; i < 8; ++i) o[i] *= al;
+    m = mn;
+  };
+  // Softmax weights P = 2^(x c2 - m) (0 for masked logits) added to the
+  // running sum and split as P = hi + lo: hi keeps the upper 16 bits of each
+  // fp32 weight (exact), lo is the remainder rounded to bf16, so hi + lo
+  // carries ~16 significant bits.
+  auto weights = [&](const float (&x)[8], float m, float& l, bf16x8_t& pop, bf16x8_t& pol, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2(fmaf(x[e], c2, -m2));
+      p[e] = fast_exp2(fmaf(x[e], c2, -m));
       if constexpr (MASK) p[e] = (x[e] == -INFINITY) ? 0.0f : p[e];
-      lsum += p[e];
+      l += p[e];
     }
-    // P = hi + lo: hi keeps the upper 16 bits of each fp32 weight (exact), lo
-    // is the remainder rounded to bf16, so hi + lo carries ~16 significant bits.
     uint32_t ph[4], pl[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -363,72 +437,124 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       pl[rr] = pack_bf16(p[2 * rr] - __uint_as_float(b0 & 0xFFFF0000u),
                          p[2 * rr + 1] - __uint_as_float(b1 & 0xFFFF0000u));
     }
-    const bf16x8_t pop = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
-    const bf16x8_t pol = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
-    // ---- O^T += V^T P^T, one MFMA per 16-column block (column 8*r16 + blk)
-    if constexpr (KV == kBF16 || KV == kMXFP4) {
-      // token-major bf16 pairs cv[e][q] = columns (8 r16 + 2q, 8 r16 + 2q + 1) of token e
-      uint32_t cv[8][4];
+    pop = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
+    pol = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+  };
+
+  // One query token on one tile: logits, the online softmax update of head
+  // n = r16 over tokens base + 16u + 4g + i, and O^T += V^T P^T, each K and V
+  // operand decoded next to its use.  MASK: rows from nvalid on are not seen
+  // (zero weight).  The running max only moves when a tile's max exceeds it
+  // by more than 2^kLazyMax (in the exp2 domain).
+  auto token_tile = [&](const Raw<KV>& rw, bf16x8_t (&kop)[2][4], const bf16x8_t (&q)[4], float& m, float& l,
+                        f32x4_t (&o)[8], int nvalid, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float x[8];
+    logits(rw, kop, q, x);
+    if constexpr (MASK) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (KV == kBF16) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) cv[e][q] = rw.v[e][q];
-        } else {
-          const float vsc = e8m0_to_f32_fast(__builtin_amdgcn_ubfe(rw.vs[e], vs_shift, 8));
-          const uint32_t w = rw.v[e][0];
-          cv[e][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 0));
-          cv[e][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 1));
-          cv[e][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 2));
-          cv[e][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 3));
-        }
+        for (int i = 0; i < 4; ++i)
+          if (16 * u + 4 * g + i >= nvalid) x[4 * u + i] = -INFINITY;
+    }
+    const float tmax2 = tile_max2(x);
+    if (__any(tmax2 > m + kLazyMax)) rescale(m, l, o, fmaxf(m, tmax2));
+    bf16x8_t pop, pol;
+    weights(x, m, l, pop, pol, mask_tag);
+    // one MFMA pair per 16-column block
+    auto pv = [&](int blk, const bf16x8_t& v) {
+      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop, o[blk], 0, 0, 0);
+      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pol, o[blk], 0, 0, 0);
+    };
+    for_v_operands<KV>(rw, vs_shift, pv);
+  };
+
+  // Every token of the chunk on one tile, phase by phase: K decoded once for
+  // the logits of all tokens, one rescale check, the weights of all, then V
+  // decoded block by block straight into every token's PV product.  The
+  // tokens' independent MFMA chains interleave, and neither all K nor all V
+  // operands are held at once.  MASK: token i sees the tile's rows below
+  // nv[i] only (none when nv[i] <= 0).
+  auto tokens_tile = [&](const Raw<KV>& rw, const int (&nv)[TW], auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float x[TW][8];
+    {
+      bf16x8_t kop[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kop[u][c] = k_operand<KV>(rw, u, c);
+#pragma unroll
+      for (int i = 0; i < TW; ++i) logits(rw, kop, qop[i], x[i]);
+    }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int i = 0; i < TW; ++i)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * u + 4 * g + e >= nv[i]) x[i][4 * u + e] = -INFINITY;
+    }
+    float tmax2[TW];
+    bool need = false;
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      tmax2[i] = tile_max2(x[i]);
+      need = need || (tmax2[i] > m2[i] + kLazyMax);
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int i = 0; i < TW; ++i)
+        if (__any(tmax2[i] > m2[i] + kLazyMax)) rescale(m2[i], lsum[i], acc[i], fmaxf(m2[i], tmax2[i]));
+    }
+    bf16x8_t pop[TW], pol[TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) weights(x[i], m2[i], lsum[i], pop[i], pol[i], mask_tag);
+    for_v_operands<KV>(rw, vs_shift, [&](int blk, const bf16x8_t& v) {
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        acc[i][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop[i], acc[i][blk], 0, 0, 0);
+        acc[i][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pol[i], acc[i][blk], 0, 0, 0);
       }
-#pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
-        const int q = blk / 2;
-        const uint32_t sel = (blk & 1) ? 0x07060302u : 0x05040100u;
-        const bf16x8_t vop = as_bf16x8(perm(cv[1][q], cv[0][q], sel), perm(cv[3][q], cv[2][q], sel),
-                                       perm(cv[5][q], cv[4][q], sel), perm(cv[7][q], cv[6][q], sel));
-        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[blk], 0, 0, 0);
-        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pol, acc[blk], 0, 0, 0);
-      }
+    });
+  };
+
+  // MASK: the tile runs past the shard end (single token: its extra tokens get
+  // zero weight).  With several tokens every token checks its own cut.
+  using Full = std::true_type;
+  using Part = std::false_type;
+  auto compute = [&](const Raw<KV>& rw, int tile, auto mask_tag) {
+    const int64_t base = s0 + (int64_t)tile * kTile;
+    if constexpr (TW == 1) {
+      bf16x8_t kop[2][4];
+      token_tile(rw, kop, qop[0], m2[0], lsum[0], acc[0], (int)(s1 - base), mask_tag);
     } else {
-      // fp8: interleave bytes of token pairs, then convert both halves
+      int nv[TW];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-#pragma unroll
-        for (int s2 = 0; s2 < 4; s2 += 2) {
-          const uint32_t sel = (s2 == 0) ? 0x05010400u : 0x07030602u;
-          uint32_t lo[4], hi[4];
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const uint32_t x2 = perm(rw.v[2 * rr + 1][q], rw.v[2 * rr][q], sel);
-            lo[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, false));
-            hi[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, true));
-          }
-          const int blk = 4 * q + s2;
-          const bf16x8_t va = as_bf16x8(lo[0], lo[1], lo[2], lo[3]);
-          const bf16x8_t vb = as_bf16x8(hi[0], hi[1], hi[2], hi[3]);
-          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, acc[blk], 0, 0, 0);
-          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pol, acc[blk], 0, 0, 0);
-          acc[blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pop, acc[blk + 1], 0, 0, 0);
-          acc[blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pol, acc[blk + 1], 0, 0, 0);
-        }
+      for (int i = 0; i < TW; ++i) {
+        const int64_t n = s1t[i] - base;         // wave-uniform
+        nv[i] = n < 0 ? 0 : (n > kTile ? kTile : (int)n);
       }
+      if (nv[0] == kTile)                        // every token sees the whole tile
+        tokens_tile(rw, nv, Part{});
+      else
+        tokens_tile(rw, nv, Full{});
     }
   };
 
   // Stream over this wave's full tiles with kRing register buffers: the loads
-  // of the next kRing-1 tiles are in flight while a tile is computed.  The
+  // of the next kRing-1 tiles are in flight while a tile is computed.  (With
+  // several query tokens a tile takes several times longer to compute, so
+  // one tile ahead is enough and leaves the registers to the tokens.)  The
   // next loads are always issued (clamped to the last full tile) so the waits
   // stay static.  A partial last tile is handled once, after the ring.
-  using Full = std::true_type;
-  using Part = std::false_type;
   const int nfull = (int)((s1 - s0) / kTile);
   if (nfull > 0) {
     auto clampt = [&](int t) { return t < nfull - 1 ? t : nfull - 1; };
     int tile = wave;
-    if constexpr (Lay::kRing == 2) {
+    if constexpr (kRing == 2) {
       Raw<KV> ra, rb;
       load(ra, clampt(tile), Full{});
       while (tile < nfull) {
@@ -441,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
         tile += kWaves;
       }
     } else {
-      static_assert(Lay::kRing == 3, "ring of 2 or 3 buffers");
+      static_assert(kRing == 3, "ring of 2 or 3 buffers");
       Raw<KV> ra, rb, rc;
       load(ra, clampt(tile), Full{});
       load(rb, clampt(tile + kWaves), Full{});
@@ -465,51 +591,56 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     load(rt, nfull, Part{});
     compute(rt, nfull, Full{});
   }
-
-  // ---- merge the four waves and write the partial
-  lsum = rows4_sum(lsum);
+  // ---- merge the four waves' states of each token and write its partial
 #pragma unroll
-  for (int blk = 0; blk < 8; ++blk) {
+  for (int i = 0; i < TW; ++i) {
+    if (i >= nq) break;
+    const float lw = rows4_sum(lsum[i]);
+    if (i > 0) __syncthreads();        // the previous token's reads are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sh_o[wave][r16][32 * g + 8 * i + blk] = acc[blk][i];
-  }
-  if (g == 0) {
-    sh_m[wave][r16] = m2;
-    sh_l[wave][r16] = lsum;
-  }
-  __syncthreads();
-  const int tid = threadIdx.x;
-  for (int idx = tid; idx < 16 * kD; idx += kThreads) {
-    const int n = idx / kD;
-    const int d = idx - n * kD;
-    float M = sh_m[0][n];
+    for (int blk = 0; blk < 8; ++blk) {
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][n]);
-    float o = 0.0f;
-    if (M != -INFINITY) {
-      float lt = 0.0f, ot = 0.0f;
+      for (int e = 0; e < 4; ++e) sh_o[wave][r16][32 * g + 8 * e + blk] = acc[i][blk][e];
+    }
+    if (g == 0) {
+      sh_m[wave][r16] = m2[i];
+      sh_l[wave][r16] = lw;
+    }
+    __syncthreads();
+    const int64_t orow0 = (((int64_t)j * a.B + b) * a.T + qt0 + i) * a.Hq + kvh * 16;   // o_part / lse_part row
+    const int tid = threadIdx.x;
+    for (int idx = tid; idx < 16 * kD; idx += kThreads) {
+      const int n = idx / kD;
+      const int d = idx - n * kD;
+      float M = sh_m[0][n];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = rescale_weight(sh_m[w][n], M);
-        lt += sh_l[w][n] * f;
-        ot += sh_o[w][n][d] * f;
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][n]);
+      float o = 0.0f;
+      if (M != -INFINITY) {
+        float lt = 0.0f, ot = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = rescale_weight(sh_m[w][n], M);
+          lt += sh_l[w][n] * f;
+          ot += sh_o[w][n][d] * f;
+        }
+        o = ot / lt * vscale;
       }
-      o = ot / lt * vscale;
+      a.o_part[(orow0 + n) * kD + d] = o;
     }
-    a.o_part[(orow0 + n) * kD + d] = o;
-  }
-  if (tid < 16) {
-    float M = sh_m[0][tid];
+    if (tid < 16) {
+      float M = sh_m[0][tid];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][tid]);
-    float lse = -INFINITY;
-    if (M != -INFINITY) {
-      float lt = 0.0f;
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][tid]);
+      float lse = -INFINITY;
+      if (M != -INFINITY) {
+        float lt = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) lt += sh_l[w][tid] * rescale_weight(sh_m[w][tid], M);
-      lse = (M + fast_log2(lt)) * kLn2;
+        for (int w = 0; w < kWaves; ++w) lt += sh_l[w][tid] * rescale_weight(sh_m[w][tid], M);
+        lse = (M + fast_log2(lt)) * kLn2;
+      }
+      a.lse_part[orow0 + tid] = lse;
     }
-    a.lse_part[orow0 + tid] = lse;
   }
 }
 
@@ -522,31 +653,40 @@ bool gqa_mfma_supports(const PartialArgs& a) {
   return a.kv_format == kBF16 || a.kv_format == kFP8 || a.kv_format == kMXFP4;
 }
 
-template <int KV, bool VS16>
-void launch_gqa(const PartialArgs& a, int64_t blocks, hipStream_t stream) {
-  if (a.layout == kPaged)
-    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+// Query tokens per workgroup: a single token streams with non-temporal
+// loads; several go two to a workgroup (more do not fit the registers
+// without spilling), the chunks of one shard running on one XCD.
+int tokens_per_workgroup(int T) { return T == 1 ? 1 : 2; }
+
+template <int KV, bool VS16, bool PAGED>
+void launch_gqa3(const PartialArgs& a, hipStream_t stream) {
+  const int tw = tokens_per_workgroup(a.T);
+  const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, (a.T + tw - 1) / tw);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (tw == 1)
+    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, PAGED, true, 1>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, PAGED, false, 2>), grid, block, 0, stream, a);
 }
 
 hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream) {
-  const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, a.T);
+  const bool paged = a.layout == kPaged;
   switch (a.kv_format) {
-    case kBF16: launch_gqa<kBF16, false>(a, blocks, stream); break;
-    case kFP8: launch_gqa<kFP8, false>(a, blocks, stream); break;
+    case kBF16:
+      paged ? launch_gqa3<kBF16, false, true>(a, stream) : launch_gqa3<kBF16, false, false>(a, stream);
+      break;
+    case kFP8:
+      paged ? launch_gqa3<kFP8, false, true>(a, stream) : launch_gqa3<kFP8, false, false>(a, stream);
+      break;
     case kMXFP4:
       // 16-token runs of scale rows are 16-byte aligned when every slab
       // starts at a multiple of 4 rows, and always in a paged pool
-      if (a.layout == kPaged)
-        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, true, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                           stream, a);
+      if (paged)
+        launch_gqa3<kMXFP4, true, true>(a, stream);
       else if (a.S_max % 4 == 0)
-        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, true, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                           stream, a);
+        launch_gqa3<kMXFP4, true, false>(a, stream);
       else
-        hipLaunchKernelGGL((gqa_mfma_kernel<kMXFP4, false, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                           stream, a);
+        launch_gqa3<kMXFP4, false, false>(a, stream);
       break;
     default:
       return hipErrorInvalidValue;
