@@ -33,14 +33,17 @@ METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S
 
 # HBM bytes per launch of the partial kernel measured with rocprofv3 counters
 # (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a plain 1 GiB
-# copy), keyed by (workload, cache layout, kvp, query tokens, sha256 prefix of the kernel code the
+# copy), keyed by (workload, cache layout (paged: with its block length),
+# kvp, query tokens, sha256 prefix of the kernel code the
 # counters were taken on).  Changed kernel code no longer matches, and the
 # bench then reports traffic as null.  Summaries are under profiles/.
 TRAFFIC = {
-    ("helix_fp8", "contiguous", 32, 1, "b385f0b82e79652f"): 17529276368,
-    ("helix_mxfp4", "contiguous", 32, 1, "b385f0b82e79652f"): 9182880567,
-    ("gqa_bf16_varlen", "contiguous", 16, 1, "b385f0b82e79652f"): 3475220072,
-    ("mla_bf16", "contiguous", 32, 1, "5a82cc7521779442"): 4900503907,
+    ("helix_fp8", "contiguous", 32, 1, "801d97422ca1c457"): 17548714407,
+    ("helix_fp8", "paged16", 32, 1, "801d97422ca1c457"): 17367899700,
+    ("helix_fp8", "contiguous", 32, 4, "801d97422ca1c457"): 17264810488,
+    ("helix_mxfp4", "contiguous", 32, 1, "801d97422ca1c457"): 9171563566,
+    ("gqa_bf16_varlen", "contiguous", 16, 1, "801d97422ca1c457"): 3536331894,
+    ("mla_bf16", "contiguous", 32, 1, "bb3c8eddaa838df9"): 4901553956,
 }
 KERNEL_SOURCES = {"bf16": "partial_gqa_mfma.hip", "fp8": "partial_gqa_mfma.hip",
                   "mxfp4": "partial_gqa_mfma.hip", "f32": "partial_valu.hip"}
@@ -259,7 +262,8 @@ def main():
     achieved = kv_bytes / (partial_avg * 1e-3) / 1e9
     peak = roofline.HBM_BYTES_PER_S / 1e9
     khash = kernel_hash(w.kv_dtype, mla=w.v_aliases_k)
-    traffic = TRAFFIC.get((w.name, args.layout, kvp, T, khash))
+    lay_key = args.layout + (str(args.block_len) if args.layout == "paged" else "")
+    traffic = TRAFFIC.get((w.name, lay_key, kvp, T, khash))
     res = {
         "metric": METRIC,
         "value": round(value, 2),
