@@ -128,8 +128,9 @@ def cpu_baseline(w, target_s=15.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first: the clocks settle over the first few dozen launches")
     ap.add_argument("--workload", default="helix_fp8")
     ap.add_argument("--kvp", type=int, default=None)
     ap.add_argument("--layout", default="contiguous", choices=["contiguous", "striped", "staggered16", "paged"],

@@ -201,3 +201,58 @@ def test_prefill_loop_matches_oracle():
         torch.cuda.synchronize()
         ref_o, ref_l = op.decode_tokens(po, T, "contiguous", kvp, q, host, L)
         gc.compare(o.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "fp8", "turn %d L=%s" % (step, tuple(L)))
+
+
+def _full_size_tokens(name, kvp, T, n_pairs=2):
+    """The full-size cache (generated on the device once) with T query tokens
+    per request; the oracle runs on sampled (request, KV head) slabs, each as a
+    one-request, one-KV-head problem regenerated on the host."""
+    import torch
+    from long_context_decode_split_amd import kvd
+    from tests.test_gpu_parity import _device_inputs
+    dev = _device_inputs(name)
+    w = dev.workload
+    wt = w.with_(q_tokens=T)
+    q = kvgen.gen_q(wt)
+    gc.log("%s T=%d kvp=%d: running the library" % (name, T, kvp))
+    p = kvd.problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, w.S_max, kvp, w.q_dtype, w.kv_dtype, 0.0, w.v_aliases_k,
+                    q_tokens=T)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o_part = torch.full((kvp, w.B, T, w.Hq, w.Dv), float("nan"), **f32)
+    lse_part = torch.full((kvp, w.B, T, w.Hq), float("nan"), **f32)
+    o = torch.full((w.B, T, w.Hq, w.Dv), float("nan"), **f32)
+    lse = torch.full((w.B, T, w.Hq), float("nan"), **f32)
+    qd = _dev(q)
+    kvd.kvd_decode_partial(p, qd, dev.k, dev.v, dev.seq_lens, o_part, lse_part)
+    kvd.kvd_lse_merge(kvp, w.B * T * w.Hq, w.Dv, o_part, lse_part, o, lse)
+    torch.cuda.synchronize()
+    o_part, lse_part, o, lse = (t.cpu().numpy() for t in (o_part, lse_part, o, lse))
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    seq = dev.seq_lens.cpu().numpy()
+    G = w.G
+    for (b, kvh) in gc.sampled_pairs(w, n_pairs):
+        L = int(seq[b])
+        gc.log("  oracle on request %d, KV head %d (L=%d, T=%d)" % (b, kvh, L, T))
+        kd, ks = kvgen.gen_kv_slab(w, "k", b, kvh)
+        vd, vs = kvgen.gen_kv_slab(w, "v", b, kvh)
+        if w.kv_dtype == "fp8":
+            ks, vs = np.asarray(ks).reshape(1, 1), np.asarray(vs).reshape(1, 1)
+        else:
+            ks, vs = ks[None, None], vs[None, None]
+        cache = {"k": kd[None, None], "k_scale": ks, "v": vd[None, None], "v_scale": vs}
+        hs = slice(kvh * G, (kvh + 1) * G)
+        sub = oracle.Problem(1, G, 1, w.Dqk, w.Dv, w.S_max, w.q_dtype, w.kv_dtype)
+        qs = np.ascontiguousarray(q[b:b + 1, :, hs])
+        ro, rl = op.decode_tokens(sub, T, "contiguous", kvp, qs, cache, [L])
+        rpo, rpl = op.decode_partials_tokens(sub, T, "contiguous", kvp, qs, cache, [L])
+        what = "%s T=%d kvp=%d b=%d kvh=%d" % (name, T, kvp, b, kvh)
+        gc.compare(o[b:b + 1, :, hs], lse[b:b + 1, :, hs], ro, rl, w.kv_dtype, what)
+        gc.compare(o_part[:, b:b + 1, :, hs], lse_part[:, b:b + 1, :, hs], rpo, rpl, w.kv_dtype, what + " partials")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,T", [("helix_fp8", 4), ("helix_mxfp4", 3)])
+def test_full_size_multi_token(name, T):
+    """The Helix shape at S = 2^20 with T query tokens, in the configuration
+    bench.py --q-tokens times (kvp = 32)."""
+    _full_size_tokens(name, 32, T)
