@@ -71,6 +71,57 @@ __device__ __forceinline__ uint32_t stream_load1(const uint8_t* p) {
   else return *p;
 }
 
+// s_waitcnt immediate that waits until at most n vector memory operations
+// remain in flight (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4 and
+// lgkmcnt 11:8 left at their maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// One direct-to-LDS 16-byte load per active lane: global address sbase + voff
+// into LDS address M0 + 16 * lane, with the non-temporal hint when NT (bytes
+// read once).  Inline asm, so the compiler does not take later LDS reads as
+// aliasing it (it would wait for every load in flight, including the prefetch
+// of the next tiles); the waits are explicit.  M0 belongs to the compiler, so
+// it is saved and restored around the load.
+template <bool NT>
+__device__ __forceinline__ void lds_dma16(uint32_t m0, const uint8_t* sbase, uint32_t voff) {
+  uint32_t m0_saved;
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved)
+        : "s"(m0), "v"(voff), "s"(sbase)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved)
+        : "s"(m0), "v"(voff), "s"(sbase)
+        : "memory");
+  }
+}
+
+// The same with a per-lane 64-bit global address (rows clamped lane by lane).
+__device__ __forceinline__ void lds_dma16_at(uint32_t m0, const uint8_t* addr) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(m0), "v"(addr)
+      : "memory");
+}
+
 // Load N bytes (N in {4, 8, 16, 32, 64}) from a 4-byte-aligned (N >= 16:
 // 16-byte aligned) global address into N/4 dwords, streaming.
 template <int N>

@@ -110,6 +110,49 @@ struct Raw {
   uint32_t vs[8];                              // MXFP4: the 4 V block exponents of each token
 };
 
+// LDS ring of the multi-token kernel: per wave, kSlots raw tiles (K rows, V
+// rows, and for MXFP4 the 4 scale bytes of each K and V row), filled by
+// direct-to-LDS loads.  A tile is 32 rows of K then 32 rows of V, each half
+// of 16 rows a contiguous copy of 16 cache rows; MXFP4 scale rows follow (K
+// tokens 0..31, then V tokens 0..31, 4 bytes each).
+template <int KV>
+struct Ring {
+  static constexpr int kRow = Layout<KV>::kRowBytes;
+  static constexpr int kSlots = KV == kBF16 ? 2 : 4;
+  static constexpr int kScaleOff = 2 * kTile * kRow;
+  static constexpr int kTileBytes = kScaleOff + (KV == kMXFP4 ? 2 * kTile * 4 : 0);
+  static constexpr int kDmaPerHalf = 16 * kRow / 1024;   // 1 KB per load instruction
+  static constexpr int kDmaPerTile = 4 * kDmaPerHalf + (KV == kMXFP4 ? 1 : 0);
+  static constexpr int kWaveBytes = kSlots * kTileBytes;
+};
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+
+// One direct-to-LDS 4-byte load per active lane from a per-lane address into
+// LDS address M0 + 4 * lane.
+__device__ __forceinline__ void lds_dma4_at(uint32_t m0, const uint8_t* addr) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(m0), "v"(addr)
+      : "memory");
+}
+
+// LDS of the final merge of the four waves' states.
+struct MergeLds {
+  float o[kWaves][16][kD + 4];
+  float m[kWaves][16];
+  float l[kWaves][16];
+};
+
 // K operand of MFMA chunk c of half-tile u (the 8 dims Layout::chunk_d(c, g)
 // of token 16u + r16), decoded to bf16.
 template <int KV>
@@ -193,15 +236,26 @@ __device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_sh
 // TW: query tokens per workgroup.  Each wave decodes a tile once and runs the
 // logits, softmax and PV product of each of the TW tokens on it; every token
 // keeps its own Q operands, softmax state and accumulator.
-template <int KV, bool VS16, bool PAGED, bool NT, int TW>
+// LDSRING: the tiles ahead wait in an LDS ring filled by direct-to-LDS loads
+// (Ring<KV>) instead of in registers, which leaves the registers to the
+// tokens and keeps several tiles in flight at one wave per SIMD.
+template <int KV, bool VS16, bool PAGED, bool NT, int TW, bool LDSRING>
 __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   using Lay = Layout<KV>;
   constexpr int64_t ROW = Lay::kRowBytes;
   constexpr int kRing = TW > 1 ? 2 : Lay::kRing;
 
-  __shared__ float sh_o[kWaves][16][kD + 4];
-  __shared__ float sh_m[kWaves][16];
-  __shared__ float sh_l[kWaves][16];
+  MergeLds* mrg;
+  uint32_t ring_lds = 0;   // LDSRING: LDS address of this wave's slots
+  if constexpr (LDSRING) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+    mrg = reinterpret_cast<MergeLds*>(dyn_lds);   // reused once the ring is drained
+    ring_lds = (uint32_t)(uintptr_t)(lds_u8*)dyn_lds +
+               (uint32_t)(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * Ring<KV>::kWaveBytes);
+  } else {
+    __shared__ MergeLds st;
+    mrg = &st;
+  }
 
   const int lane = threadIdx.x & 63;
   // wave index as a scalar, so everything derived from it stays wave-uniform
@@ -544,52 +598,163 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     }
   };
 
-  // Stream over this wave's full tiles with kRing register buffers: the loads
-  // of the next kRing-1 tiles are in flight while a tile is computed.  (With
-  // several query tokens a tile takes several times longer to compute, so
-  // one tile ahead is enough and leaves the registers to the tokens.)  The
-  // next loads are always issued (clamped to the last full tile) so the waits
-  // stay static.  A partial last tile is handled once, after the ring.
   const int nfull = (int)((s1 - s0) / kTile);
-  if (nfull > 0) {
-    auto clampt = [&](int t) { return t < nfull - 1 ? t : nfull - 1; };
-    int tile = wave;
-    if constexpr (kRing == 2) {
-      Raw<KV> ra, rb;
-      load(ra, clampt(tile), Full{});
-      while (tile < nfull) {
-        load(rb, clampt(tile + kWaves), Full{});
-        compute(ra, tile, Part{});
-        tile += kWaves;
-        if (tile >= nfull) break;
-        load(ra, clampt(tile + kWaves), Full{});
-        compute(rb, tile, Part{});
-        tile += kWaves;
+  if constexpr (LDSRING) {
+    using R = Ring<KV>;
+    // Direct-to-LDS loads of tile `tile` into slot sl.  Full tile: each half
+    // is 16 consecutive rows, copied 1 KB per instruction from a wave-uniform
+    // base.  Partial tile (CLAMP): rows past the shard's last one are clamped,
+    // lane by lane.  The scale rows of an MXFP4 tile: one 4-byte load per
+    // lane, lanes 0..31 K, 32..63 V.
+    auto issue = [&](int tile, int sl, auto clamp_tag) {
+      constexpr bool CLAMP = decltype(clamp_tag)::value;
+      const int64_t base = s0 + (int64_t)tile * kTile;
+      const uint32_t dst = ring_lds + (uint32_t)(sl * R::kTileBytes);
+      int64_t hr[2] = {0, 0};
+      if constexpr (!CLAMP) {
+        hr[0] = hrow(base);
+        hr[1] = hrow(base + 16);
       }
-    } else {
-      static_assert(kRing == 3, "ring of 2 or 3 buffers");
-      Raw<KV> ra, rb, rc;
-      load(ra, clampt(tile), Full{});
-      load(rb, clampt(tile + kWaves), Full{});
-      while (tile < nfull) {
-        load(rc, clampt(tile + 2 * kWaves), Full{});
-        compute(ra, tile, Part{});
-        tile += kWaves;
-        if (tile >= nfull) break;
-        load(ra, clampt(tile + 2 * kWaves), Full{});
-        compute(rb, tile, Part{});
-        tile += kWaves;
-        if (tile >= nfull) break;
-        load(rb, clampt(tile + 2 * kWaves), Full{});
-        compute(rc, tile, Part{});
-        tile += kWaves;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int n = 0; n < R::kDmaPerHalf; ++n) {
+          const uint32_t off = (uint32_t)(n * 1024 + 16 * lane);   // byte of the half-tile
+          const uint32_t m0k = __builtin_amdgcn_readfirstlane(dst + (uint32_t)(u * 16 * ROW + n * 1024));
+          const uint32_t m0v = m0k + (uint32_t)(kTile * ROW);
+          if constexpr (CLAMP) {
+            int64_t t = base + 16 * u + off / ROW;
+            t = t < last ? t : last;
+            const int64_t pr = hrow(t) * ROW + off % ROW;
+            lds_dma16_at(m0k, kdata + pr);
+            lds_dma16_at(m0v, vdata + pr);
+          } else {
+            lds_dma16<NT>(m0k, kdata + hr[u] * ROW, off);
+            lds_dma16<NT>(m0v, vdata + hr[u] * ROW, off);
+          }
+        }
+      }
+      if constexpr (KV == kMXFP4) {
+        const int tk = lane & 31;
+        int64_t pr;
+        if constexpr (CLAMP) {
+          int64_t t = base + tk;
+          t = t < last ? t : last;
+          pr = hrow(t);
+        } else {
+          pr = (tk < 16 ? hr[0] : hr[1]) + (tk & 15);
+        }
+        lds_dma4_at(__builtin_amdgcn_readfirstlane(dst + (uint32_t)R::kScaleOff),
+                    (lane < 32 ? ksdata : vsdata) + pr * SROW);
+      }
+    };
+    // The raw registers of slot sl, in the lane layout of the register loads.
+    auto fetch = [&](Raw<KV>& rw, int sl) {
+      const lds_u8* sp = (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)(sl * R::kTileBytes));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int i = 0; i < Lay::kKLoads; ++i) {
+          const u32x4_t v = *(const lds_u32x4*)(sp + u * 16 * ROW + koff + 64 * i);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) rw.k[u][4 * i + w] = v[w];
+        }
+        if constexpr (KV == kMXFP4) rw.ks[u] = sp[R::kScaleOff + 64 * u + ksoff];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const lds_u8* p = sp + kTile * ROW + (16 * (e / 4) + (e % 4)) * ROW + voff;
+        if constexpr (Lay::kVBytes == 16) {
+          const u32x4_t v = *(const lds_u32x4*)p;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) rw.v[e][w] = v[w];
+        } else if constexpr (Lay::kVBytes == 8) {
+          const u32x2_t v = *(const lds_u32x2*)p;
+          rw.v[e][0] = v[0];
+          rw.v[e][1] = v[1];
+        } else {
+          rw.v[e][0] = *(const lds_u32*)p;
+        }
+        if constexpr (KV == kMXFP4)
+          rw.vs[e] = *(const lds_u32*)(sp + R::kScaleOff + 4 * kTile + 4 * (16 * (e / 4) + 4 * g + (e % 4)));
+      }
+    };
+    // Every vector memory operation in flight from here on is a ring load.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (nfull > 0) {
+      auto clampt = [&](int t) { return t < nfull - 1 ? t : nfull - 1; };
+#pragma unroll
+      for (int k = 0; k < R::kSlots - 1; ++k) issue(clampt(wave + k * kWaves), k, Part{});
+      int sl = 0;
+      for (int tile = wave; tile < nfull; tile += kWaves) {
+        // refill the slot read in the previous iteration, kSlots - 1 tiles ahead
+        issue(clampt(tile + (R::kSlots - 1) * kWaves), sl == 0 ? R::kSlots - 1 : sl - 1, Part{});
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((R::kSlots - 1) * R::kDmaPerTile));
+        asm volatile("" ::: "memory");
+        Raw<KV> rw;
+        fetch(rw, sl);
+        compute(rw, tile, Part{});
+        sl = sl + 1 == R::kSlots ? 0 : sl + 1;
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+    }
+    if (nfull < ntiles && nfull % kWaves == wave) {
+      issue(nfull, 0, Full{});
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+      Raw<KV> rt;
+      fetch(rt, 0);
+      compute(rt, nfull, Full{});
+    }
+    __syncthreads();   // every wave is done with its slots before the merge reuses them
+  } else {
+    // Stream over this wave's full tiles with kRing register buffers: the loads
+    // of the next kRing-1 tiles are in flight while a tile is computed.  (With
+    // several query tokens a tile takes several times longer to compute, so
+    // one tile ahead is enough and leaves the registers to the tokens.)  The
+    // next loads are always issued (clamped to the last full tile) so the waits
+    // stay static.  A partial last tile is handled once, after the ring.
+    if (nfull > 0) {
+      auto clampt = [&](int t) { return t < nfull - 1 ? t : nfull - 1; };
+      int tile = wave;
+      if constexpr (kRing == 2) {
+        Raw<KV> ra, rb;
+        load(ra, clampt(tile), Full{});
+        while (tile < nfull) {
+          load(rb, clampt(tile + kWaves), Full{});
+          compute(ra, tile, Part{});
+          tile += kWaves;
+          if (tile >= nfull) break;
+          load(ra, clampt(tile + kWaves), Full{});
+          compute(rb, tile, Part{});
+          tile += kWaves;
+        }
+      } else {
+        static_assert(kRing == 3, "ring of 2 or 3 buffers");
+        Raw<KV> ra, rb, rc;
+        load(ra, clampt(tile), Full{});
+        load(rb, clampt(tile + kWaves), Full{});
+        while (tile < nfull) {
+          load(rc, clampt(tile + 2 * kWaves), Full{});
+          compute(ra, tile, Part{});
+          tile += kWaves;
+          if (tile >= nfull) break;
+          load(ra, clampt(tile + 2 * kWaves), Full{});
+          compute(rb, tile, Part{});
+          tile += kWaves;
+          if (tile >= nfull) break;
+          load(rb, clampt(tile + 2 * kWaves), Full{});
+          compute(rc, tile, Part{});
+          tile += kWaves;
+        }
       }
     }
-  }
-  if (nfull < ntiles && nfull % kWaves == wave) {
-    Raw<KV> rt;
-    load(rt, nfull, Part{});
-    compute(rt, nfull, Full{});
+    if (nfull < ntiles && nfull % kWaves == wave) {
+      Raw<KV> rt;
+      load(rt, nfull, Part{});
+      compute(rt, nfull, Full{});
+    }
   }
   // ---- merge the four waves' states of each token and write its partial
 #pragma unroll
@@ -600,11 +765,11 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sh_o[wave][r16][32 * g + 8 * e + blk] = acc[i][blk][e];
+      for (int e = 0; e < 4; ++e) mrg->o[wave][r16][32 * g + 8 * e + blk] = acc[i][blk][e];
     }
     if (g == 0) {
-      sh_m[wave][r16] = m2[i];
-      sh_l[wave][r16] = lw;
+      mrg->m[wave][r16] = m2[i];
+      mrg->l[wave][r16] = lw;
     }
     __syncthreads();
     const int64_t orow0 = (((int64_t)j * a.B + b) * a.T + qt0 + i) * a.Hq + kvh * 16;   // o_part / lse_part row
@@ -612,31 +777,31 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     for (int idx = tid; idx < 16 * kD; idx += kThreads) {
       const int n = idx / kD;
       const int d = idx - n * kD;
-      float M = sh_m[0][n];
+      float M = mrg->m[0][n];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][n]);
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg->m[w][n]);
       float o = 0.0f;
       if (M != -INFINITY) {
         float lt = 0.0f, ot = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float f = rescale_weight(sh_m[w][n], M);
-          lt += sh_l[w][n] * f;
-          ot += sh_o[w][n][d] * f;
+          const float f = rescale_weight(mrg->m[w][n], M);
+          lt += mrg->l[w][n] * f;
+          ot += mrg->o[w][n][d] * f;
         }
         o = ot / lt * vscale;
       }
       a.o_part[(orow0 + n) * kD + d] = o;
     }
     if (tid < 16) {
-      float M = sh_m[0][tid];
+      float M = mrg->m[0][tid];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][tid]);
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg->m[w][tid]);
       float lse = -INFINITY;
       if (M != -INFINITY) {
         float lt = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) lt += sh_l[w][tid] * rescale_weight(sh_m[w][tid], M);
+        for (int w = 0; w < kWaves; ++w) lt += mrg->l[w][tid] * rescale_weight(mrg->m[w][tid], M);
         lse = (M + fast_log2(lt)) * kLn2;
       }
       a.lse_part[orow0 + tid] = lse;
@@ -654,43 +819,67 @@ bool gqa_mfma_supports(const PartialArgs& a) {
 }
 
 // Query tokens per workgroup: a single token streams with non-temporal
-// loads; several go two to a workgroup (more do not fit the registers
-// without spilling), the chunks of one shard running on one XCD.
-int tokens_per_workgroup(int T) { return T == 1 ? 1 : 2; }
+// loads; two share each decoded tile with their tiles ahead in registers.  A
+// bf16 cache, whose tiles are twice as large, runs three or more tokens four
+// to a workgroup with the tiles ahead in an LDS ring (measured faster there;
+// slower for the fp8 and MXFP4 caches, whose decode work dominates).  The
+// chunks of one shard run on one XCD.
+int tokens_per_workgroup(int T, int kv) {
+  if (T == 1) return 1;
+  return (kv == kBF16 && T >= 3) ? 4 : 2;
+}
 
 template <int KV, bool VS16, bool PAGED>
-void launch_gqa3(const PartialArgs& a, hipStream_t stream) {
-  const int tw = tokens_per_workgroup(a.T);
+hipError_t launch_gqa3(const PartialArgs& a, hipStream_t stream) {
+  const int tw = tokens_per_workgroup(a.T, KV);
   const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, (a.T + tw - 1) / tw);
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (tw == 1)
-    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, PAGED, true, 1>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, PAGED, false, 2>), grid, block, 0, stream, a);
+  if (tw == 1) {
+    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, PAGED, true, 1, false>), grid, block, 0, stream, a);
+  } else if (tw == 2) {
+    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, PAGED, false, 2, false>), grid, block, 0, stream, a);
+  } else if constexpr (KV == kBF16) {
+    constexpr size_t kLds = (size_t)kWaves * Ring<KV>::kWaveBytes;
+    static_assert(kLds >= sizeof(MergeLds) && kLds <= 160 * 1024, "LDS ring budget");
+    auto fn = gqa_mfma_kernel<KV, VS16, PAGED, false, 4, true>;
+    static bool configured = false;
+    if (!configured) {
+      const hipError_t e =
+          hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+      if (e != hipSuccess) return e;
+      configured = true;
+    }
+    hipLaunchKernelGGL(fn, grid, block, kLds, stream, a);
+  } else {
+    return hipErrorInvalidValue;   // no four-token instance for this format
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream) {
   const bool paged = a.layout == kPaged;
+  hipError_t e;
   switch (a.kv_format) {
     case kBF16:
-      paged ? launch_gqa3<kBF16, false, true>(a, stream) : launch_gqa3<kBF16, false, false>(a, stream);
+      e = paged ? launch_gqa3<kBF16, false, true>(a, stream) : launch_gqa3<kBF16, false, false>(a, stream);
       break;
     case kFP8:
-      paged ? launch_gqa3<kFP8, false, true>(a, stream) : launch_gqa3<kFP8, false, false>(a, stream);
+      e = paged ? launch_gqa3<kFP8, false, true>(a, stream) : launch_gqa3<kFP8, false, false>(a, stream);
       break;
     case kMXFP4:
       // 16-token runs of scale rows are 16-byte aligned when every slab
       // starts at a multiple of 4 rows, and always in a paged pool
       if (paged)
-        launch_gqa3<kMXFP4, true, true>(a, stream);
+        e = launch_gqa3<kMXFP4, true, true>(a, stream);
       else if (a.S_max % 4 == 0)
-        launch_gqa3<kMXFP4, true, false>(a, stream);
+        e = launch_gqa3<kMXFP4, true, false>(a, stream);
       else
-        launch_gqa3<kMXFP4, false, false>(a, stream);
+        e = launch_gqa3<kMXFP4, false, false>(a, stream);
       break;
     default:
       return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

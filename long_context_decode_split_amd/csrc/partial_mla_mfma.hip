@@ -80,34 +80,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// s_waitcnt immediate that waits until at most n vector memory operations
-// remain in flight (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4 and
-// lgkmcnt 11:8 left at their maxima).
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 static_assert(2 * kLoads < 64, "vmcnt range");
 
 // Token (within a 16-token half-tile) held by MFMA row m = 4a + i:
 // a = 0 -> 0,2,4,6; a = 1 -> 1,3,5,7; a = 2 -> 8,..,14; a = 3 -> 9,..,15.
 __device__ __forceinline__ int perm16(int m) { return ((m >> 2) & 1) + 2 * (m & 3) + 8 * (m >> 3); }
-
-// One direct-to-LDS 16-byte load per active lane: global address sbase + voff
-// into LDS address M0 + 16 * lane, with the non-temporal hint (every cached
-// byte is read once).  Inline asm, so the compiler does not take later LDS
-// reads as aliasing it (it would wait for every load in flight, including the
-// prefetch of the next tiles); the waits are explicit.  M0 belongs to the
-// compiler, so it is saved and restored around the load.
-__device__ __forceinline__ void lds_dma16(uint32_t m0, const uint8_t* sbase, uint32_t voff) {
-  uint32_t m0_saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3 nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(m0_saved)
-      : "s"(m0), "v"(voff), "s"(sbase)
-      : "memory");
-}
 
 // PAGED: rows are found through the block table (paged cache layout).
 template <bool PAGED>
@@ -189,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
 #pragma unroll
       for (int k = 0; k < kRowsPerWave; ++k) {
         const int r = kRowsPerWave * wave + k;
-        lds_dma16(__builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(r * kMainStride * 16)),
+        lds_dma16<true>(__builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(r * kMainStride * 16)),
                   src + k * kRowBytes, (uint32_t)(lane * 16));
       }
 #pragma unroll
@@ -197,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
         const int r0 = kRowsPerWave * wave + 4 * h;
         const uint32_t m0 =
             __builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(kMainBytes + r0 * kTailStride * 16));
-        if (lane < 36) lds_dma16(m0, src + 4 * h * kRowBytes, (uint32_t)(tl_row * kRowBytes) + tl_off);
+        if (lane < 36) lds_dma16<true>(m0, src + 4 * h * kRowBytes, (uint32_t)(tl_row * kRowBytes) + tl_off);
       }
     } else {
       // last tile: rows clamped to the shard's last token
@@ -206,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
         const int r = kRowsPerWave * wave + k;
         int64_t row = base + r;
         row = row < last ? row : last;
-        lds_dma16(__builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(r * kMainStride * 16)),
+        lds_dma16<true>(__builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(r * kMainStride * 16)),
                   kdata + hrow(row) * kRowBytes, (uint32_t)(lane * 16));
       }
 #pragma unroll
@@ -221,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
         int64_t row = row0 + tl_row;
         row = row < last ? row : last;
         const uint32_t off = (uint32_t)((row - rb) * kRowBytes) + tl_off;
-        if (lane < 36) lds_dma16(m0, kdata + hrow(rb) * kRowBytes, off);
+        if (lane < 36) lds_dma16<true>(m0, kdata + hrow(rb) * kRowBytes, off);
       }
     }
   };

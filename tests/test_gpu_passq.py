@@ -117,6 +117,18 @@ def test_token_counts_valu_f32():
         _check(w, T, "contiguous", kvp, S, [(160, 40)], seed=9)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "mxfp4"])
+def test_token_counts_ring_formats(kv):
+    """Odd token counts: bf16 runs them four to a workgroup with the LDS ring,
+    MXFP4 two to a workgroup, here with S_max % 4 != 0 (scale rows of a slab
+    not 16-byte aligned)."""
+    kvp = 3
+    S = 190 if kv == "mxfp4" else 192
+    w = _wl(kv, S=S, Hq=32, Hkv=2, D=128)
+    for T in (3, 9):
+        _check(w, T, "contiguous", kvp, S, [(S, 77), (19, S - 1)], seed=11)
+
+
 def test_mla_multi_token_paged():
     kvp, T, S = 5, 3, 192
     w = _wl("bf16", S=S, **SHAPES["mla"])
