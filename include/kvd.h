@@ -38,7 +38,9 @@
  * Conventions for every entry point:
  *  - Ownership: every pointer argument (except `p`, which is host memory) is a
  *    caller-owned DEVICE pointer.  The library never allocates, frees or
- *    synchronizes; it keeps no state between calls and is reentrant.
+ *    synchronizes; it keeps no state between calls and is reentrant (apart
+ *    from raising, once per process and thread-safely, the dynamic-LDS limit
+ *    of the kernels that use more than 64 KB of it).
  *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the null
  *    stream) and the call returns without waiting for it.
  *  - Layouts: contiguous row-major.  q [B,T,Hq,Dqk]; k.data [B,Hkv,S_max,Dqk];

@@ -18,11 +18,13 @@
 // the output error stays near fp32 level even for short shards.
 //
 // Work split: one workgroup of 4 waves per (shard j, request b, KV head,
-// query token t; a single-token decode has t = 0 only); wave
-// w takes the shard's 32-token tiles w, w+4, w+8, ... and keeps the loads of
-// its next one (bf16) or two (fp8, MXFP4: smaller tiles) tiles in flight while
-// computing the current one, so enough bytes are outstanding to cover HBM
-// latency at 2 waves per SIMD.  Lane (r, g) = (lane % 16, lane / 16):
+// chunk of query tokens: one token for a single-token decode, two or four for
+// a multi-token turn); wave w takes the shard's 32-token tiles w, w+4, w+8, ...
+// and, for one token, keeps the loads of its next one (bf16) or two (fp8,
+// MXFP4: smaller tiles) tiles in flight while computing the current one, so
+// enough bytes are outstanding to cover HBM latency at 2-3 waves per SIMD.
+// Several tokens share every decoded tile (see TW below).
+// Lane (r, g) = (lane % 16, lane / 16):
 //  * K: lane (r, g) loads token r of each 16-token half-tile, bytes
 //    [64i + 16g, 64i + 16g + 16) of the row for each 16-byte load i, so each
 //    load instruction reads 64 contiguous bytes of 16 rows.
@@ -842,13 +844,11 @@ hipError_t launch_gqa3(const PartialArgs& a, hipStream_t stream) {
     constexpr size_t kLds = (size_t)kWaves * Ring<KV>::kWaveBytes;
     static_assert(kLds >= sizeof(MergeLds) && kLds <= 160 * 1024, "LDS ring budget");
     auto fn = gqa_mfma_kernel<KV, VS16, PAGED, false, 4, true>;
-    static bool configured = false;
-    if (!configured) {
-      const hipError_t e =
-          hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-      if (e != hipSuccess) return e;
-      configured = true;
-    }
+    // more than 64 KB of dynamic LDS: raise the kernel's limit once (the
+    // initialization of a local static is thread-safe)
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(fn, grid, block, kLds, stream, a);
   } else {
     return hipErrorInvalidValue;   // no four-token instance for this format

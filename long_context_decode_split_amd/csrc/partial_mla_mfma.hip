@@ -406,15 +406,17 @@ bool mla_mfma_supports(const PartialArgs& a) {
 }
 
 hipError_t launch_partial_mla_mfma(const PartialArgs& a, hipStream_t stream) {
-  static bool configured = false;
-  if (!configured) {
+  // more than 64 KB of dynamic LDS: raise both instances' limit once (the
+  // initialization of a local static is thread-safe)
+  static const hipError_t attr = [] {
     for (const void* fn : {reinterpret_cast<const void*>(mla_mfma_kernel<false>),
                            reinterpret_cast<const void*>(mla_mfma_kernel<true>)}) {
-      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
       if (e != hipSuccess) return e;
     }
-    configured = true;
-  }
+    return hipSuccess;
+  }();
+  if (attr != hipSuccess) return attr;
   const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, a.T);
   if (a.layout == kPaged)
     hipLaunchKernelGGL(mla_mfma_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), kSmemBytes, stream, a);

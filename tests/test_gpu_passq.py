@@ -268,3 +268,24 @@ def test_full_size_multi_token(name, T):
     """The Helix shape at S = 2^20 with T query tokens, in the configuration
     bench.py --q-tokens times (kvp = 32)."""
     _full_size_tokens(name, 32, T)
+
+
+def test_append_tokens_latent_alias():
+    """T = 3 new latent rows per request (V aliases K): only K is written, bit
+    for bit, on a staggered cache."""
+    import torch
+    from long_context_decode_split_amd import kvd
+    T, kvp, S = 3, 2, 40
+    w = _wl("bf16", B=2, Hq=128, Hkv=1, D=576, Dv=512, S=S, alias=True)
+    host = _zero_cache(w, "staggered16", kvp, S)
+    dk = _dev(host["k"])
+    p = kvd.problem(w.B, w.Hq, 1, 576, 512, S, kvp, "bf16", "bf16", 0.0, True, layout="staggered16", q_tokens=T)
+    po = oracle.Problem(w.B, w.Hq, 1, 576, 512, S, "bf16", "bf16", True)
+    rng = np.random.default_rng(4)
+    for step in range(8):
+        kn = rng.standard_normal((w.B, T, 1, 576)).astype(np.float32)
+        pos = np.array([T * step, 70 - T * step], dtype=np.int32)
+        op.append_tokens(po, T, "staggered16", kvp, host, pos, kn, None)
+        kvd.kvd_append_kv(p, _dev(kn), None, _dev(pos), (dk, None), None)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(dk, host["k"]), host["k"])
