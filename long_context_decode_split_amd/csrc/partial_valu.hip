@@ -23,7 +23,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRows = kThreads / 16;
 
-template <int KV, int DQK, int DV, int HC, bool QBF16, bool ALIAS>
+// HC: query heads per workgroup.  DEPTH: tokens per row whose loads are in
+// flight together (2 for full grids; 8 for small ones, where every row has
+// many tokens to walk and load latency, not throughput, sets the time).
+template <int KV, int DQK, int DV, int HC, bool QBF16, bool ALIAS, int DEPTH>
 __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
   constexpr int EK = DQK / 16;
   constexpr int EV = DV / 16;
@@ -155,15 +158,15 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
   };
 
   int64_t t = s0 + row;
-  for (; t + kRows < s1; t += 2 * kRows) {
-    uint32_t kw0[KW], vw0[VW], kw1[KW], vw1[VW];
-    float ks0, vs0, ks1, vs1;
-    load(t, kw0, vw0, &ks0, &vs0);
-    load(t + kRows, kw1, vw1, &ks1, &vs1);
-    process(kw0, vw0, ks0, vs0);
-    process(kw1, vw1, ks1, vs1);
+  for (; t + (DEPTH - 1) * kRows < s1; t += DEPTH * kRows) {
+    uint32_t kw[DEPTH][KW], vw[DEPTH][VW];
+    float ks[DEPTH], vs[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load(t + d * kRows, kw[d], vw[d], &ks[d], &vs[d]);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) process(kw[d], vw[d], ks[d], vs[d]);
   }
-  if (t < s1) {
+  for (; t < s1; t += kRows) {
     uint32_t kw0[KW], vw0[VW];
     float ks0, vs0;
     load(t, kw0, vw0, &ks0, &vs0);
@@ -240,36 +243,49 @@ constexpr int head_chunk() {
   return D <= 128 ? 8 : 4;
 }
 
+// A grid of fewer workgroups than the chip has compute units (a few shards of
+// a few requests) runs one query head per workgroup with eight tokens in
+// flight per row: more workgroups, each with a short latency-bound walk.
+constexpr int64_t kSmallGrid = 256;
+
+int64_t grid_units(const PartialArgs& a, int hc) {
+  const int G = a.Hq / a.Hkv;
+  return (int64_t)a.kvp * a.B * a.Hkv * ((G + hc - 1) / hc) * a.T;
+}
+
+bool small_grid(const PartialArgs& a) { return grid_units(a, a.Dqk <= 128 ? 8 : 4) < kSmallGrid; }
+
 using KernelFn = void (*)(PartialArgs);
 
 template <int KV, int D, bool QBF16, bool ALIAS>
-KernelFn pick3() {
-  return partial_valu_kernel<KV, D, D, head_chunk<D>(), QBF16, ALIAS>;
+KernelFn pick3(bool small) {
+  if (small) return partial_valu_kernel<KV, D, D, 1, QBF16, ALIAS, 8>;
+  return partial_valu_kernel<KV, D, D, head_chunk<D>(), QBF16, ALIAS, 2>;
 }
 
 template <int KV, int D>
-KernelFn pick2(bool qbf16, bool alias) {
-  if (qbf16) return alias ? pick3<KV, D, true, true>() : pick3<KV, D, true, false>();
-  return alias ? pick3<KV, D, false, true>() : pick3<KV, D, false, false>();
+KernelFn pick2(bool qbf16, bool alias, bool small) {
+  if (qbf16) return alias ? pick3<KV, D, true, true>(small) : pick3<KV, D, true, false>(small);
+  return alias ? pick3<KV, D, false, true>(small) : pick3<KV, D, false, false>(small);
 }
 
 template <int KV>
-KernelFn pick1(int D, bool qbf16, bool alias) {
+KernelFn pick1(int D, bool qbf16, bool alias, bool small) {
   if constexpr (KV != kMXFP4) {
-    if (D == 64) return pick2<KV, 64>(qbf16, alias);
+    if (D == 64) return pick2<KV, 64>(qbf16, alias, small);
   }
-  if (D == 128) return pick2<KV, 128>(qbf16, alias);
-  if (D == 256) return pick2<KV, 256>(qbf16, alias);
+  if (D == 128) return pick2<KV, 128>(qbf16, alias, small);
+  if (D == 256) return pick2<KV, 256>(qbf16, alias, small);
   return nullptr;
 }
 
 KernelFn pick(const PartialArgs& a) {
-  const bool qb = a.q_bf16 != 0, al = a.v_aliases_k != 0;
+  const bool qb = a.q_bf16 != 0, al = a.v_aliases_k != 0, sm = small_grid(a);
   switch (a.kv_format) {
-    case kF32: return pick1<kF32>(a.Dqk, qb, al);
-    case kBF16: return pick1<kBF16>(a.Dqk, qb, al);
-    case kFP8: return pick1<kFP8>(a.Dqk, qb, al);
-    case kMXFP4: return pick1<kMXFP4>(a.Dqk, qb, al);
+    case kF32: return pick1<kF32>(a.Dqk, qb, al, sm);
+    case kBF16: return pick1<kBF16>(a.Dqk, qb, al, sm);
+    case kFP8: return pick1<kFP8>(a.Dqk, qb, al, sm);
+    case kMXFP4: return pick1<kMXFP4>(a.Dqk, qb, al, sm);
     default: return nullptr;
   }
 }
@@ -285,7 +301,7 @@ hipError_t launch_partial_valu(const PartialArgs& a, hipStream_t stream) {
   KernelFn fn = pick(a);
   if (fn == nullptr) return hipErrorInvalidValue;
   const int G = a.Hq / a.Hkv;
-  const int hc = a.Dqk <= 128 ? 8 : 4;
+  const int hc = small_grid(a) ? 1 : (a.Dqk <= 128 ? 8 : 4);
   const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv * ((G + hc - 1) / hc), a.T);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -48,6 +48,19 @@ def test_sweep(kv, D, G):
             gc.check_full(w, kvp)
 
 
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8", "mxfp4"])
+def test_valu_full_grid(kv):
+    """Grids of at least one workgroup per compute unit take the vector-ALU
+    kernel's many-heads-per-workgroup variant (the small cases above take the
+    one-head variant): 8 requests x 4 KV heads x 16 shards."""
+    for D, G, q_dtype in ((64, 4, "bf16"), (128, 8, "f32"), (128, 16, "f32"), (128, 1, "bf16")):
+        if kv == "mxfp4" and D == 64:
+            continue
+        w = W("valu_grid_%s_d%d_g%d" % (kv, D, G), B=8, Hq=G * 4, Hkv=4, Dqk=D, Dv=D, S_max=400, kv_dtype=kv,
+              q_dtype=q_dtype, seq_lens=(400, 1, 17, 399, 0, 250, 33, 128), seed=300 + G + D)
+        gc.check_full(w, 16)
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
 def test_group16_long_ragged(kv):
     """G=16 at a few thousand tokens with lengths off every tile boundary."""
