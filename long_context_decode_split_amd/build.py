@@ -47,8 +47,28 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
+EXAMPLE_SRC = os.path.join(PKG, "examples", "decode_from_c.c")
+EXAMPLE = os.path.join(PKG, "examples", "decode_from_c")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_example(verbose: bool = False) -> str:
+    """Compile the plain-C caller of the ABI (gcc, host code only) against
+    libkvd.so and the HIP runtime; returns its path."""
+    tmp = EXAMPLE + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", os.path.join(ROCM, "include"), EXAMPLE_SRC, "-L", PKG, "-lkvd", "-L", os.path.join(ROCM, "lib"),
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/..:" + os.path.join(ROCM, "lib"), "-o", tmp]
+    subprocess.check_call(cmd)
+    os.replace(tmp, EXAMPLE)
+    if verbose:
+        print("built", EXAMPLE)
+    return EXAMPLE
+
+
 def build(extra=(), jobs: int = 8, verbose: bool = False) -> str:
-    """Compile all sources and link libkvd.so; returns its path."""
+    """Compile all sources and link libkvd.so, then the C example; returns the
+    library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
@@ -58,6 +78,7 @@ def build(extra=(), jobs: int = 8, verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_example(verbose)
     return LIB
 
 
