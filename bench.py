@@ -145,6 +145,9 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip timing kvd_append_kv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step (partial pass + merge) captured once into a HIP graph "
+                         "and replayed; reported under 'graph'")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that each start with the last-level cache flushed "
                          "(for workloads whose cache fits in it); reported under 'cold'")
@@ -324,6 +327,27 @@ def main():
                 if i >= args.warmup:
                     app.append(e[0].elapsed_time(e[1]))
         res["append_us_median"] = round(median(app) * 1e3, 2)
+    if args.graph:
+        # The same step captured once and replayed: launch overhead leaves the
+        # timed region (it matters for the small, latency-bound workloads).
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gs.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            ge.record(stream)
+            torch.cuda.synchronize()
+        g_ms = gs.elapsed_time(ge) / args.steps
+        res["graph"] = {"us_per_step": round(g_ms * 1e3, 2), "value": round(kv_bytes / (g_ms * 1e-3) / 1e9, 2),
+                        "unit": "GB/s", "note": "the step replayed from a HIP graph; 'value' above is eager"}
+        del g
     if args.cold:
         # Each step starts after a 1 GiB write that evicts the cache from the
         # 256 MB last-level cache; only the step itself is inside the events.
