@@ -46,6 +46,14 @@ TRAFFIC = {
     ("gqa_bf16_varlen", "contiguous", 16, 4, "9ebe81f619d0abdc"): 3475748754,
     ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 4901559411,
 }
+# Fraction of the partial kernel's SIMD cycles with the matrix cores busy,
+# SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs), from a
+# rocprofv3 --pmc run; same keys as TRAFFIC.
+MFMA_BUSY = {
+    ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 0.5503,
+    ("helix_mxfp4", "contiguous", 32, 1, "9ebe81f619d0abdc"): 0.3209,
+    ("helix_fp8", "contiguous", 32, 1, "9ebe81f619d0abdc"): 0.1849,
+}
 KERNEL_SOURCES = {"bf16": "partial_gqa_mfma.hip", "fp8": "partial_gqa_mfma.hip",
                   "mxfp4": "partial_gqa_mfma.hip", "f32": "partial_valu.hip"}
 
@@ -375,6 +383,7 @@ def main():
         executed = roofline.attention_flops(w.Hq, seq, w.Dqk, 2 * w.Dv)
         t = partial_avg * 1e-3
         res["roofline"]["mfma"] = {
+            "busy_frac_counter": MFMA_BUSY.get((w.name, lay_key, kvp, T, khash)),
             "peak_tflops": roofline.MFMA_BF16_FLOPS / 1e12,
             "algorithmic_tflops": round(flops / t / 1e12, 2),
             "algorithmic_frac": round(flops / t / roofline.MFMA_BF16_FLOPS, 4),
