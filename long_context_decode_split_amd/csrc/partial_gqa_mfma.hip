@@ -3,19 +3,25 @@
 // With 16 query heads sharing one KV head, every cached K and V element feeds
 // 16 multiply-adds, which is more arithmetic per HBM byte than the fp32 vector
 // ALUs can sustain for fp8 or MXFP4 caches.  The 16 heads of the group are
-// exactly the 16-wide dimension of the gfx950 bf16 matrix instruction
-// v_mfma_f32_16x16x32_bf16, so both contractions run on it:
+// exactly the 16-wide dimension of the gfx950 matrix instructions, so both
+// contractions run on them:
 //
-//   S^T[token, head] = K_tile[token, :] . Q[head, :]          (K = 128 = 4 MFMAs)
+//   S^T[token, head] = K_tile[token, :] . Q[head, :]
 //   O^T[dv, head]   += V_tile^T[dv, token] . P^T[token, head] (32 tokens, 8 column
 //                                                              blocks x (hi, lo) = 16 MFMAs)
 //
-// Cache elements are decoded to bf16 in registers (bf16 as is; OCP E4M3 and
-// MXFP4 with the hardware converters, exactly) and Q is the bf16 query as
-// given, so the logits are exact products summed in fp32.  The softmax weights
-// P = exp2(logit - running max) are fp32; the PV product takes them as a bf16
-// pair hi + lo (two MFMAs), which keeps ~16 significant bits instead of 8, so
-// the output error stays near fp32 level even for short shards.
+// The logits of a bf16 cache take four v_mfma_f32_16x16x32_bf16 per 16
+// tokens.  An fp8 or MXFP4 K tile is not decoded at all: its bytes are the
+// A operand of the block-scaled v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 with
+// unit scales, or E2M1 with the cache's own E8M0 block exponents), and the
+// bf16 query is the B operand as two E4M3 parts with power-of-two scales
+// whose sum reproduces every query element that matters exactly (split_query),
+// so the logits are exact products summed in fp32 in every format.  V is
+// decoded to bf16 in registers with the hardware converters (exact).  The
+// softmax weights P = exp2(logit - running max) are fp32; the PV product
+// takes them as a bf16 pair hi + lo (two MFMAs), which keeps ~16 significant
+// bits instead of 8, so the output error stays near fp32 level even for short
+// shards.
 //
 // Work split: one workgroup of 4 waves per (shard j, request b, KV head,
 // chunk of query tokens: one token for a single-token decode, two or four for
@@ -23,7 +29,7 @@
 // and, for one token, keeps the loads of its next one (bf16) or two (fp8,
 // MXFP4: smaller tiles) tiles in flight while computing the current one, so
 // enough bytes are outstanding to cover HBM latency at 2-3 waves per SIMD.
-// Several tokens share every decoded tile (see TW below).
+// Several tokens share every loaded tile (see TW below).
 // Lane (r, g) = (lane % 16, lane / 16):
 //  * K: lane (r, g) loads token r of each 16-token half-tile, bytes
 //    [64i + 16g, 64i + 16g + 16) of the row for each 16-byte load i, so each
@@ -51,6 +57,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -86,21 +93,22 @@ struct Layout<kBF16> {
   // first d of MFMA chunk c for lane group g
   __device__ static constexpr int chunk_d(int c, int g) { return 32 * c + 8 * g; }
 };
+// kFmt: the A operand format code of the block-scaled MFMA (cbsz).
 template <>
 struct Layout<kFP8> {
+  static constexpr int kFmt = 0;        // E4M3; lane (r, g) holds dims 16g.. and 64+16g..
   static constexpr int kRing = 3;
   static constexpr int kKLoads = 2;
   static constexpr int kVBytes = 8;
   static constexpr int kRowBytes = 128;
-  __device__ static constexpr int chunk_d(int c, int g) { return 64 * (c / 2) + 16 * g + 8 * (c % 2); }
 };
 template <>
 struct Layout<kMXFP4> {
+  static constexpr int kFmt = 4;        // E2M1; lane (r, g) holds dims 32g .. 32g+31
   static constexpr int kRing = 3;
   static constexpr int kKLoads = 1;
   static constexpr int kVBytes = 4;
   static constexpr int kRowBytes = 64;
-  __device__ static constexpr int chunk_d(int c, int g) { return 32 * g + 8 * c; }
 };
 
 // Raw (undecoded) registers of one 32-token tile for one lane.
@@ -109,22 +117,18 @@ struct Raw {
   uint32_t k[2][Layout<KV>::kKLoads * 4];      // two half-tiles
   uint32_t v[8][Layout<KV>::kVBytes / 4];      // 8 tokens
   uint32_t ks[2];                              // MXFP4: K block exponent per half-tile
-  uint32_t vs[8];                              // MXFP4: the 4 V block exponents of each token
+  uint32_t vs[2];                              // MXFP4: byte `lane` of the half-tile's V exponents
 };
 
-// LDS ring of the multi-token kernel: per wave, kSlots raw tiles (K rows, V
-// rows, and for MXFP4 the 4 scale bytes of each K and V row), filled by
-// direct-to-LDS loads.  A tile is 32 rows of K then 32 rows of V, each half
-// of 16 rows a contiguous copy of 16 cache rows; MXFP4 scale rows follow (K
-// tokens 0..31, then V tokens 0..31, 4 bytes each).
-template <int KV>
+// LDS ring of the multi-token kernel (bf16 cache): per wave, kSlots raw
+// tiles filled by direct-to-LDS loads.  A tile is 32 rows of K then 32 rows
+// of V, each half of 16 rows a contiguous copy of 16 cache rows.
 struct Ring {
-  static constexpr int kRow = Layout<KV>::kRowBytes;
-  static constexpr int kSlots = KV == kBF16 ? 2 : 4;
-  static constexpr int kScaleOff = 2 * kTile * kRow;
-  static constexpr int kTileBytes = kScaleOff + (KV == kMXFP4 ? 2 * kTile * 4 : 0);
+  static constexpr int kRow = Layout<kBF16>::kRowBytes;
+  static constexpr int kSlots = 2;
+  static constexpr int kTileBytes = 2 * kTile * kRow;
   static constexpr int kDmaPerHalf = 16 * kRow / 1024;   // 1 KB per load instruction
-  static constexpr int kDmaPerTile = 4 * kDmaPerHalf + (KV == kMXFP4 ? 1 : 0);
+  static constexpr int kDmaPerTile = 4 * kDmaPerHalf;
   static constexpr int kWaveBytes = kSlots * kTileBytes;
 };
 
@@ -133,21 +137,6 @@ typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
-// One direct-to-LDS 4-byte load per active lane from a per-lane address into
-// LDS address M0 + 4 * lane.
-__device__ __forceinline__ void lds_dma4_at(uint32_t m0, const uint8_t* addr) {
-  uint32_t m0_saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(m0_saved)
-      : "s"(m0), "v"(addr)
-      : "memory");
-}
-
 // LDS of the final merge of the four waves' states.
 struct MergeLds {
   float o[kWaves][16][kD + 4];
@@ -155,36 +144,101 @@ struct MergeLds {
   float l[kWaves][16];
 };
 
-// K operand of MFMA chunk c of half-tile u (the 8 dims Layout::chunk_d(c, g)
-// of token 16u + r16), decoded to bf16.
+// bf16 K operand of MFMA chunk c of half-tile u: the 8 dims
+// Layout<kBF16>::chunk_d(c, g) of token 16u + r16.
+__device__ __forceinline__ bf16x8_t k_operand(const Raw<kBF16>& rw, int u, int c) {
+  return as_bf16x8(rw.k[u][4 * c], rw.k[u][4 * c + 1], rw.k[u][4 * c + 2], rw.k[u][4 * c + 3]);
+}
+
+// The K bytes of half-tile u as the A operand of the block-scaled MFMA: an
+// fp8 lane holds 32 E4M3 bytes, an MXFP4 lane 16 bytes (32 E2M1 nibbles, the
+// upper half of the operand unused).
 template <int KV>
-__device__ __forceinline__ bf16x8_t k_operand(const Raw<KV>& rw, int u, int c) {
-  if constexpr (KV == kBF16) {
-    return as_bf16x8(rw.k[u][4 * c], rw.k[u][4 * c + 1], rw.k[u][4 * c + 2], rw.k[u][4 * c + 3]);
-  } else if constexpr (KV == kFP8) {
-    const uint32_t w0 = rw.k[u][2 * c], w1 = rw.k[u][2 * c + 1];
-    return __builtin_bit_cast(
-        bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))});
-  } else {
-    const float ksc = e8m0_to_f32_fast(rw.ks[u]);
-    const uint32_t w = rw.k[u][c];
-    return __builtin_bit_cast(
-        bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 0)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 1)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 2)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, ksc, 3))});
+__device__ __forceinline__ i32x8_t k_bytes(const Raw<KV>& rw, int u) {
+  i32x8_t a;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) a[w] = w < 4 * Layout<KV>::kKLoads ? (int)rw.k[u][w] : 0;
+  return a;
+}
+
+// The query of head n as the B operand of v_mfma_scale_f32_16x16x128_f8f6f4
+// (fp8 and MXFP4 caches).  With 8-bit operands lane group g of that
+// instruction covers the contraction indices {16g .. 16g+15, 64+16g .. 64+16g+15}
+// (bytes 0-15, 16-31) and supplies the E8M0 scale of index block g
+// (32g .. 32g+31); with a 4-bit A operand lane group g covers 32g .. 32g+31.
+// One scale per head, so the per-lane scales agree whatever the grouping.
+// The bf16 query is split as q = hi 2^sh + lo 2^sl, hi and lo OCP E4M3 and
+// round-to-nearest: sh puts the head's largest |q| in [128, 256) hi units and
+// sl = sh - 4.  Where |q| >= 2^(sh-6) (hi normal), the residual q - hi 2^sh is
+// a multiple of q's ulp of at most half an E4M3 ulp of q, so it has at most
+// 4 significant bits and lo holds it exactly: hi 2^sh + lo 2^sl = q.  Smaller
+// elements (below 2^-13 of the head's largest |q|) are off by at most half an
+// E4M3 subnormal step of lo, 2^(sl-10) = 2^(sh-14).
+struct QSplit {
+  i32x8_t hi, lo;
+  int sh, sl;   // E8M0 scale bytes (exponent + 127)
+};
+
+__device__ __forceinline__ QSplit split_query(const uint16_t* qrow, int g) {
+  float x[32];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 64 * h + 16 * g + 8 * k);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[16 * h + 8 * k + 2 * e] = __uint_as_float(w[e] << 16);
+        x[16 * h + 8 * k + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    }
   }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = rows4_max(amax);   // the head's 128 dims sit in its 4 lane groups
+  // floor(log2(amax)) from the exponent field (amax = 0 or fp32-subnormal: the
+  // clamp below takes over)
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127;
+  int sh = e - 7;
+  sh = sh < -123 ? -123 : (sh > 120 ? 120 : sh);
+  const int sl = sh - 4;
+  const float inv_h = __uint_as_float((uint32_t)(127 - sh) << 23);   // 2^-sh, exact
+  QSplit r;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float y[4], z[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = x[4 * w + k] * inv_h;
+    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    hw = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], hw, true);
+    const f32x2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)hw, 1.0f, false);
+    const f32x2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)hw, 1.0f, true);
+    // residual in lo units (exact: y - hi is on y's grid, 16 a power of two)
+    z[0] = (y[0] - h01[0]) * 16.0f;
+    z[1] = (y[1] - h01[1]) * 16.0f;
+    z[2] = (y[2] - h23[0]) * 16.0f;
+    z[3] = (y[3] - h23[1]) * 16.0f;
+    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
+    lw = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], lw, true);
+    r.hi[w] = hw;
+    r.lo[w] = lw;
+  }
+  r.sh = sh + 127;
+  r.sl = sl + 127;
+  return r;
 }
 
 // V^T operands of the 8 16-column blocks of the PV product, decoded to bf16:
 // f(blk, op) is called for each block as soon as its operand is ready.  The
 // operand of block blk holds the lane's column of that block for the 8 tokens
 // {4g + i, 16 + 4g + i}, in the k order of the P^T operand.
+// MXFP4: lane L of the wave holds the V exponent of (token 16u + L / 4,
+// column block L % 4) in rw.vs[u]; vs_lane is the byte address (for
+// ds_bpermute) of the lane holding this lane's block (r / 4) of token 4g.
 template <int KV, class F>
-__device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_shift, F&& f) {
+__device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_lane, F&& f) {
   if constexpr (KV == kBF16 || KV == kMXFP4) {
     // token-major bf16 pairs cv[e][q] = columns (8 r16 + 2q, 8 r16 + 2q + 1) of token e
     uint32_t cv[8][4];
@@ -194,7 +248,9 @@ __device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_sh
 #pragma unroll
         for (int q = 0; q < 4; ++q) cv[e][q] = rw.v[e][q];
       } else {
-        const float vsc = e8m0_to_f32_fast(__builtin_amdgcn_ubfe(rw.vs[e], vs_shift, 8));
+        // token 16 (e / 4) + 4g + e % 4 sits 4 (e % 4) lanes past token 4g
+        const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(vs_lane + 16 * (e % 4)), (int)rw.vs[e / 4]);
+        const float vsc = e8m0_to_f32_fast(x);
         const uint32_t w = rw.v[e][0];
         cv[e][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 0));
         cv[e][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 1));
@@ -230,7 +286,6 @@ __device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_sh
   }
 }
 
-// VS16 (MXFP4 only): every 16-token run of V scale rows is 16-byte aligned.
 // PAGED: rows are found through the block table (paged cache layout).
 // NT: cache loads carry the non-temporal hint (one query token: every byte is
 // read once); several query tokens read each byte once per token chunk, from
@@ -239,10 +294,11 @@ __device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_sh
 // logits, softmax and PV product of each of the TW tokens on it; every token
 // keeps its own Q operands, softmax state and accumulator.
 // LDSRING: the tiles ahead wait in an LDS ring filled by direct-to-LDS loads
-// (Ring<KV>) instead of in registers, which leaves the registers to the
+// (Ring, bf16 cache) instead of in registers, which leaves the registers to the
 // tokens and keeps several tiles in flight at one wave per SIMD.
-template <int KV, bool VS16, bool PAGED, bool NT, int TW, bool LDSRING>
-__global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
+template <int KV, bool PAGED, bool NT, int TW, bool LDSRING>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV != kBF16 && TW == 1 ? 3 : 1)))
+void gqa_mfma_kernel(PartialArgs a) {
   using Lay = Layout<KV>;
   constexpr int64_t ROW = Lay::kRowBytes;
   constexpr int kRing = TW > 1 ? 2 : Lay::kRing;
@@ -253,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
     mrg = reinterpret_cast<MergeLds*>(dyn_lds);   // reused once the ring is drained
     ring_lds = (uint32_t)(uintptr_t)(lds_u8*)dyn_lds +
-               (uint32_t)(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * Ring<KV>::kWaveBytes);
+               (uint32_t)(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * Ring::kWaveBytes);
   } else {
     __shared__ MergeLds st;
     mrg = &st;
@@ -318,17 +374,24 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   }
   const float c2 = a.scale_log2 * kscale;  // raw logit -> log2 domain
 
-  // Q^T operands: lane (n, g) holds head n, the 8 d of chunk c for group g,
-  // of each token of the chunk (a token past the end of T loads the last one's).
+  // Q^T operands of each token of the chunk (a token past the end of T loads
+  // the last one's): bf16 cache, lane (n, g) holds head n, the 8 d of chunk c
+  // for group g; fp8 and MXFP4 caches, the two E4M3 parts of split_query.
+  constexpr bool SCALED = KV != kBF16;
   bf16x8_t qop[TW][4];
+  QSplit qs[TW];
 #pragma unroll
   for (int i = 0; i < TW; ++i) {
     const int qt = qt0 + (i < nq ? i : nq - 1);
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.T + qt) * a.Hq + kvh * 16 + r16) * kD;
+    if constexpr (SCALED) {
+      qs[i] = split_query(qrow, g);
+    } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + Lay::chunk_d(c, g));
-      qop[i][c] = as_bf16x8(v.x, v.y, v.z, v.w);
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qrow + Lay::chunk_d(c, g));
+        qop[i][c] = as_bf16x8(v.x, v.y, v.z, v.w);
+      }
     }
   }
 
@@ -350,11 +413,10 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   const uint32_t koff = (uint32_t)(r16 * ROW + 16 * g);
   const uint32_t voff = (uint32_t)(4 * g * ROW + Lay::kVBytes * r16);
   const uint32_t ksoff = (uint32_t)(r16 * (kD / 32) + g);
-  // MXFP4 V scales: the 4 exponent bytes of tokens 4g .. 4g+3 (and 16 + ...)
-  // are 16 contiguous bytes, one load each when every slab's scale array is
-  // 16-byte aligned (VS16: S_max % 4 == 0); the lane picks byte r16 / 4.
-  const uint32_t vsoff = (uint32_t)(4 * g * (kD / 32));
-  const uint32_t vs_shift = (uint32_t)(8 * (r16 / 4));
+  // MXFP4 V scales: the 64 exponent bytes of a half-tile (16 tokens x 4
+  // column blocks) are one byte per lane, lane L holding byte L; the lane that
+  // holds this lane's block r16 / 4 of token 4g is 16g + r16 / 4.
+  const uint32_t vs_lane = (uint32_t)(4 * (16 * g + r16 / 4));
 
   // FULL: every row of the tile is inside the shard (no clamping needed).
   // Each 16-token half-tile is 16 consecutive physical rows starting at
@@ -399,20 +461,12 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     if constexpr (KV == kMXFP4) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        if constexpr (FULL && VS16) {
-          const u32x4_t v = stream_load16<NT>(vsdata + hr[u] * SROW + vsoff);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) rw.vs[4 * u + i] = v[i];
-        } else if constexpr (FULL) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) rw.vs[4 * u + i] = stream_load4<NT>(vsdata + hr[u] * SROW + vsoff + 4 * i);
+        if constexpr (FULL) {
+          rw.vs[u] = stream_load1<NT>(vsdata + hr[u] * SROW + lane);
         } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            int64_t t = base + 16 * u + 4 * g + i;
-            t = t < last ? t : last;
-            rw.vs[4 * u + i] = stream_load4<NT>(vsdata + hrow(t) * SROW);
-          }
+          int64_t t = base + 16 * u + lane / 4;
+          t = t < last ? t : last;
+          rw.vs[u] = stream_load1<NT>(vsdata + hrow(t) * SROW + (lane & 3));
         }
       }
     }
@@ -442,19 +496,29 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     }
   };
 
-  // Logits S^T = K Q^T of one query token for the two half-tiles, as 8
-  // values per lane: head n = r16, tokens base + 16u + 4g + i at x[4u + i].
-  auto logits = [&](const Raw<KV>& rw, bf16x8_t (&kop)[2][4], const bf16x8_t (&q)[4], float (&x)[8]) {
+  // Logits S^T = K Q^T of query token i of the chunk for the two half-tiles,
+  // as 8 values per lane: head n = r16, tokens base + 16u + 4g + i at x[4u + i].
+  // bf16: kop holds the K operands (filled here for one token); fp8 and
+  // MXFP4: two block-scaled MFMAs per half-tile (query parts hi and lo) on the
+  // raw K bytes.
+  auto logits = [&](const Raw<KV>& rw, bf16x8_t (&kop)[2][4], int i, float (&x)[8]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (SCALED) {
+        const i32x8_t ka = k_bytes<KV>(rw, u);
+        const int ksc = KV == kMXFP4 ? (int)rw.ks[u] : 127;   // E8M0 1.0 for fp8
+        s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qs[i].hi, s, Lay::kFmt, 0, 0, ksc, 0, qs[i].sh);
+        s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qs[i].lo, s, Lay::kFmt, 0, 0, ksc, 0, qs[i].sl);
+      } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if constexpr (TW == 1) kop[u][c] = k_operand<KV>(rw, u, c);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u][c], q[c], s, 0, 0, 0);
+        for (int c = 0; c < 4; ++c) {
+          if constexpr (TW == 1) kop[u][c] = k_operand(rw, u, c);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u][c], qop[i][c], s, 0, 0, 0);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * u + i] = s[i];
+      for (int e = 0; e < 4; ++e) x[4 * u + e] = s[e];
     }
   };
   // Tile max of the lane's head in the log2 domain.
@@ -502,11 +566,11 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
   // operand decoded next to its use.  MASK: rows from nvalid on are not seen
   // (zero weight).  The running max only moves when a tile's max exceeds it
   // by more than 2^kLazyMax (in the exp2 domain).
-  auto token_tile = [&](const Raw<KV>& rw, bf16x8_t (&kop)[2][4], const bf16x8_t (&q)[4], float& m, float& l,
-                        f32x4_t (&o)[8], int nvalid, auto mask_tag) {
+  auto token_tile = [&](const Raw<KV>& rw, bf16x8_t (&kop)[2][4], float& m, float& l, f32x4_t (&o)[8], int nvalid,
+                        auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     float x[8];
-    logits(rw, kop, q, x);
+    logits(rw, kop, 0, x);
     if constexpr (MASK) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -523,11 +587,12 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
       o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop, o[blk], 0, 0, 0);
       o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pol, o[blk], 0, 0, 0);
     };
-    for_v_operands<KV>(rw, vs_shift, pv);
+    for_v_operands<KV>(rw, vs_lane, pv);
   };
 
-  // Every token of the chunk on one tile, phase by phase: K decoded once for
-  // the logits of all tokens, one rescale check, the weights of all, then V
+  // Every token of the chunk on one tile, phase by phase: the K operands (bf16:
+  // repacked once; fp8, MXFP4: the raw bytes) for the logits of all tokens, one
+  // rescale check, the weights of all, then V
   // decoded block by block straight into every token's PV product.  The
   // tokens' independent MFMA chains interleave, and neither all K nor all V
   // operands are held at once.  MASK: token i sees the tile's rows below
@@ -537,12 +602,14 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     float x[TW][8];
     {
       bf16x8_t kop[2][4];
+      if constexpr (!SCALED) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kop[u][c] = k_operand<KV>(rw, u, c);
+          for (int c = 0; c < 4; ++c) kop[u][c] = k_operand(rw, u, c);
+      }
 #pragma unroll
-      for (int i = 0; i < TW; ++i) logits(rw, kop, qop[i], x[i]);
+      for (int i = 0; i < TW; ++i) logits(rw, kop, i, x[i]);
     }
     if constexpr (MASK) {
 #pragma unroll
@@ -568,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     bf16x8_t pop[TW], pol[TW];
 #pragma unroll
     for (int i = 0; i < TW; ++i) weights(x[i], m2[i], lsum[i], pop[i], pol[i], mask_tag);
-    for_v_operands<KV>(rw, vs_shift, [&](int blk, const bf16x8_t& v) {
+    for_v_operands<KV>(rw, vs_lane, [&](int blk, const bf16x8_t& v) {
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
         acc[i][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop[i], acc[i][blk], 0, 0, 0);
@@ -585,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
     const int64_t base = s0 + (int64_t)tile * kTile;
     if constexpr (TW == 1) {
       bf16x8_t kop[2][4];
-      token_tile(rw, kop, qop[0], m2[0], lsum[0], acc[0], (int)(s1 - base), mask_tag);
+      token_tile(rw, kop, m2[0], lsum[0], acc[0], (int)(s1 - base), mask_tag);
     } else {
       int nv[TW];
 #pragma unroll
@@ -602,12 +669,12 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
 
   const int nfull = (int)((s1 - s0) / kTile);
   if constexpr (LDSRING) {
-    using R = Ring<KV>;
+    static_assert(KV == kBF16, "LDS ring: bf16 cache only");
+    using R = Ring;
     // Direct-to-LDS loads of tile `tile` into slot sl.  Full tile: each half
     // is 16 consecutive rows, copied 1 KB per instruction from a wave-uniform
     // base.  Partial tile (CLAMP): rows past the shard's last one are clamped,
-    // lane by lane.  The scale rows of an MXFP4 tile: one 4-byte load per
-    // lane, lanes 0..31 K, 32..63 V.
+    // lane by lane.
     auto issue = [&](int tile, int sl, auto clamp_tag) {
       constexpr bool CLAMP = decltype(clamp_tag)::value;
       const int64_t base = s0 + (int64_t)tile * kTile;
@@ -636,19 +703,6 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
           }
         }
       }
-      if constexpr (KV == kMXFP4) {
-        const int tk = lane & 31;
-        int64_t pr;
-        if constexpr (CLAMP) {
-          int64_t t = base + tk;
-          t = t < last ? t : last;
-          pr = hrow(t);
-        } else {
-          pr = (tk < 16 ? hr[0] : hr[1]) + (tk & 15);
-        }
-        lds_dma4_at(__builtin_amdgcn_readfirstlane(dst + (uint32_t)R::kScaleOff),
-                    (lane < 32 ? ksdata : vsdata) + pr * SROW);
-      }
     };
     // The raw registers of slot sl, in the lane layout of the register loads.
     auto fetch = [&](Raw<KV>& rw, int sl) {
@@ -661,7 +715,6 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) rw.k[u][4 * i + w] = v[w];
         }
-        if constexpr (KV == kMXFP4) rw.ks[u] = sp[R::kScaleOff + 64 * u + ksoff];
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -677,8 +730,6 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
         } else {
           rw.v[e][0] = *(const lds_u32*)p;
         }
-        if constexpr (KV == kMXFP4)
-          rw.vs[e] = *(const lds_u32*)(sp + R::kScaleOff + 4 * kTile + 4 * (16 * (e / 4) + 4 * g + (e % 4)));
       }
     };
     // Every vector memory operation in flight from here on is a ring load.
@@ -732,8 +783,7 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
           compute(rb, tile, Part{});
           tile += kWaves;
         }
-      } else {
-        static_assert(kRing == 3, "ring of 2 or 3 buffers");
+      } else if constexpr (kRing == 3) {
         Raw<KV> ra, rb, rc;
         load(ra, clampt(tile), Full{});
         load(rb, clampt(tile + kWaves), Full{});
@@ -748,6 +798,29 @@ __global__ __launch_bounds__(kThreads) void gqa_mfma_kernel(PartialArgs a) {
           if (tile >= nfull) break;
           load(rb, clampt(tile + 2 * kWaves), Full{});
           compute(rc, tile, Part{});
+          tile += kWaves;
+        }
+      } else {
+        static_assert(kRing == 4, "ring of 2, 3 or 4 buffers");
+        Raw<KV> ra, rb, rc, rd;
+        load(ra, clampt(tile), Full{});
+        load(rb, clampt(tile + kWaves), Full{});
+        load(rc, clampt(tile + 2 * kWaves), Full{});
+        while (tile < nfull) {
+          load(rd, clampt(tile + 3 * kWaves), Full{});
+          compute(ra, tile, Part{});
+          tile += kWaves;
+          if (tile >= nfull) break;
+          load(ra, clampt(tile + 3 * kWaves), Full{});
+          compute(rb, tile, Part{});
+          tile += kWaves;
+          if (tile >= nfull) break;
+          load(rb, clampt(tile + 3 * kWaves), Full{});
+          compute(rc, tile, Part{});
+          tile += kWaves;
+          if (tile >= nfull) break;
+          load(rc, clampt(tile + 3 * kWaves), Full{});
+          compute(rd, tile, Part{});
           tile += kWaves;
         }
       }
@@ -831,19 +904,19 @@ int tokens_per_workgroup(int T, int kv) {
   return (kv == kBF16 && T >= 3) ? 4 : 2;
 }
 
-template <int KV, bool VS16, bool PAGED>
+template <int KV, bool PAGED>
 hipError_t launch_gqa3(const PartialArgs& a, hipStream_t stream) {
   const int tw = tokens_per_workgroup(a.T, KV);
   const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, (a.T + tw - 1) / tw);
   const dim3 grid((unsigned)blocks), block(kThreads);
   if (tw == 1) {
-    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, PAGED, true, 1, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, true, 1, false>), grid, block, 0, stream, a);
   } else if (tw == 2) {
-    hipLaunchKernelGGL((gqa_mfma_kernel<KV, VS16, PAGED, false, 2, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, false, 2, false>), grid, block, 0, stream, a);
   } else if constexpr (KV == kBF16) {
-    constexpr size_t kLds = (size_t)kWaves * Ring<KV>::kWaveBytes;
+    constexpr size_t kLds = (size_t)kWaves * Ring::kWaveBytes;
     static_assert(kLds >= sizeof(MergeLds) && kLds <= 160 * 1024, "LDS ring budget");
-    auto fn = gqa_mfma_kernel<KV, VS16, PAGED, false, 4, true>;
+    auto fn = gqa_mfma_kernel<KV, PAGED, false, 4, true>;
     // more than 64 KB of dynamic LDS: raise the kernel's limit once (the
     // initialization of a local static is thread-safe)
     static const hipError_t attr =
@@ -861,20 +934,13 @@ hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream) {
   hipError_t e;
   switch (a.kv_format) {
     case kBF16:
-      e = paged ? launch_gqa3<kBF16, false, true>(a, stream) : launch_gqa3<kBF16, false, false>(a, stream);
+      e = paged ? launch_gqa3<kBF16, true>(a, stream) : launch_gqa3<kBF16, false>(a, stream);
       break;
     case kFP8:
-      e = paged ? launch_gqa3<kFP8, false, true>(a, stream) : launch_gqa3<kFP8, false, false>(a, stream);
+      e = paged ? launch_gqa3<kFP8, true>(a, stream) : launch_gqa3<kFP8, false>(a, stream);
       break;
     case kMXFP4:
-      // 16-token runs of scale rows are 16-byte aligned when every slab
-      // starts at a multiple of 4 rows, and always in a paged pool
-      if (paged)
-        e = launch_gqa3<kMXFP4, true, true>(a, stream);
-      else if (a.S_max % 4 == 0)
-        e = launch_gqa3<kMXFP4, true, false>(a, stream);
-      else
-        e = launch_gqa3<kMXFP4, false, false>(a, stream);
+      e = paged ? launch_gqa3<kMXFP4, true>(a, stream) : launch_gqa3<kMXFP4, false>(a, stream);
       break;
     default:
       return hipErrorInvalidValue;
