@@ -70,8 +70,8 @@ def test_group16_long_ragged(kv):
 
 
 def test_mxfp4_scale_rows_not_16b_aligned():
-    """S_max % 4 != 0 leaves each slab's E8M0 scale array off 16-byte alignment,
-    which selects the kernel variant that loads V scales 4 bytes at a time."""
+    """S_max % 4 != 0 leaves each slab's E8M0 scale array off 16-byte (and
+    4-byte) alignment; the kernels load scale bytes one per lane."""
     w = W("mxfp4_smax1001", B=2, Hq=32, Hkv=2, S_max=1001, seq_lens=(1001, 37), kv_dtype="mxfp4", seed=13)
     for kvp in (1, 3, 16):
         gc.check_full(w, kvp)
@@ -157,6 +157,39 @@ def test_rising_logits(kind):
         ref_o, ref_l = oracle.decode(p, *args)
         gc.compare(o_part, lse_part, ref_po, ref_pl, w.kv_dtype, "%s ramp kvp=%d partials" % (kind, kvp))
         gc.compare(o, lse, ref_o, ref_l, w.kv_dtype, "%s ramp kvp=%d merged" % (kind, kvp))
+
+
+@pytest.mark.parametrize("kv", ["fp8", "mxfp4"])
+def test_query_dynamic_range(kv):
+    """Queries far from N(0, 1): per-head magnitudes from 2^-40 to 2^4, elements
+    within a head spread over 2^-30 of the head's largest, a head of zeros and
+    bf16 subnormals.  The fp8 and MXFP4 logits take the query as two E4M3
+    parts with one exponent pair per head, exact above 2^-13 of the head's
+    largest |q| and within 2^-21 of it below; every head must still match."""
+    import numpy as np
+    import torch
+    from kvgen.device import upload
+    import oracle
+    w = W("qrange_%s" % kv, B=2, Hq=32, Hkv=2, S_max=300, seq_lens=(300, 77), kv_dtype=kv, seed=41)
+    inp = kvgen.make_inputs(w)
+    rng = np.random.default_rng(17)
+    q = rng.standard_normal((w.B, w.Hq, w.Dqk))
+    q *= np.exp2(-rng.uniform(0.0, 30.0, q.shape))            # spread inside each head
+    q *= np.exp2(rng.uniform(-40.0, 4.0, (w.B, w.Hq, 1)))     # per-head magnitude
+    q[0, 3] = 0.0                                              # all-zero head
+    q[1, 5] = rng.standard_normal(w.Dqk) * 2.0 ** -130         # bf16 subnormals
+    q[1, 6, :64] = 0.0                                         # half a head zero
+    bits = torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    inp.q[...] = bits
+    dev = upload(inp)
+    p = oracle.Problem.from_workload(w)
+    args = (inp.q, inp.k_data, inp.k_scale, inp.v_data, inp.v_scale, inp.seq_lens)
+    for kvp in (1, 5):
+        o_part, lse_part, o, lse = gc.run_library(dev, kvp)
+        ref_po, ref_pl = oracle.decode_partials(p, kvp, *args)
+        ref_o, ref_l = oracle.decode(p, *args)
+        gc.compare(o_part, lse_part, ref_po, ref_pl, kv, "%s qrange kvp=%d partials" % (kv, kvp))
+        gc.compare(o, lse, ref_o, ref_l, kv, "%s qrange kvp=%d merged" % (kv, kvp))
 
 
 def test_repeat_runs_bitwise_identical():
