@@ -80,6 +80,30 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Raw buffer resource (four SGPRs) over `bytes` bytes at a wave-uniform
+// address.  Loads through it take a 32-bit lane offset plus an immediate, so a
+// full tile needs no 64-bit per-lane address arithmetic; offsets at or past
+// `bytes` would read zeros instead of memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
+}
+template <bool NT>
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0));
+}
+template <bool NT>
+__device__ __forceinline__ u32x2_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, NT ? 2 : 0));
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, NT ? 2 : 0);
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, NT ? 2 : 0);
+}
+
 template <int KV>
 struct Layout;
 
@@ -425,73 +449,76 @@ void gqa_mfma_kernel(PartialArgs a) {
   auto load = [&](Raw<KV>& rw, int tile, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int64_t base = s0 + (int64_t)tile * kTile;
-    int64_t hr[2] = {0, 0};
     if constexpr (FULL) {
-      hr[0] = hrow(base);
-      hr[1] = hrow(base + 16);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint8_t* p;
-      int64_t pt = 0;
-      if constexpr (FULL) {
-        p = kdata + hr[u] * ROW + koff;
-      } else {
-        int64_t t = base + 16 * u + r16;
-        t = t < last ? t : last;
-        pt = hrow(t);
-        p = kdata + pt * ROW + 16 * g;
-      }
-#pragma unroll
-      for (int i = 0; i < Lay::kKLoads; ++i) {
-        const u32x4_t v = stream_load16<NT>(p + 64 * i);
-        rw.k[u][4 * i + 0] = v[0];
-        rw.k[u][4 * i + 1] = v[1];
-        rw.k[u][4 * i + 2] = v[2];
-        rw.k[u][4 * i + 3] = v[3];
-      }
-      if constexpr (KV == kMXFP4) {
-        if constexpr (FULL) {
-          rw.ks[u] = stream_load1<NT>(ksdata + hr[u] * SROW + ksoff);
-        } else {
-          rw.ks[u] = stream_load1<NT>(ksdata + pt * SROW + g);
-        }
-      }
-    }
-    if constexpr (KV == kMXFP4) {
+      // every load of a half-tile through one buffer resource over its 16 rows
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        if constexpr (FULL) {
-          rw.vs[u] = stream_load1<NT>(vsdata + hr[u] * SROW + lane);
-        } else {
-          int64_t t = base + 16 * u + lane / 4;
-          t = t < last ? t : last;
-          rw.vs[u] = stream_load1<NT>(vsdata + hrow(t) * SROW + (lane & 3));
+        const int64_t hr = hrow(base + 16 * u);
+        const auto rk = tile_rsrc(kdata + hr * ROW, 16 * ROW);
+#pragma unroll
+        for (int i = 0; i < Lay::kKLoads; ++i) {
+          const u32x4_t v = buf_load16<NT>(rk, koff + 64 * i);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) rw.k[u][4 * i + w] = v[w];
+        }
+        const auto rv = tile_rsrc(vdata + hr * ROW, 16 * ROW);
+#pragma unroll
+        for (int e = 4 * u; e < 4 * u + 4; ++e) {   // token 16u + 4g + e%4
+          const uint32_t off = voff + (uint32_t)((e % 4) * ROW);
+          if constexpr (Lay::kVBytes == 16) {
+            const u32x4_t v = buf_load16<NT>(rv, off);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) rw.v[e][w] = v[w];
+          } else if constexpr (Lay::kVBytes == 8) {
+            const u32x2_t v = buf_load8<NT>(rv, off);
+            rw.v[e][0] = v[0];
+            rw.v[e][1] = v[1];
+          } else {
+            rw.v[e][0] = buf_load4<NT>(rv, off);
+          }
+        }
+        if constexpr (KV == kMXFP4) {
+          rw.ks[u] = buf_load1<NT>(tile_rsrc(ksdata + hr * SROW, 16 * SROW), ksoff);
+          rw.vs[u] = buf_load1<NT>(tile_rsrc(vsdata + hr * SROW, 16 * SROW), (uint32_t)lane);
         }
       }
-    }
+    } else {
+      // partial tile: rows past the shard's last one are clamped, lane by lane
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint8_t* p;
-      if constexpr (FULL) {
-        p = vdata + (hr[e / 4] + (e % 4)) * ROW + voff;   // token 16 (e/4) + 4g + e%4
-      } else {
+      for (int u = 0; u < 2; ++u) {
+        int64_t t = base + 16 * u + r16;
+        t = t < last ? t : last;
+        const int64_t pt = hrow(t);
+        const uint8_t* p = kdata + pt * ROW + 16 * g;
+#pragma unroll
+        for (int i = 0; i < Lay::kKLoads; ++i) {
+          const u32x4_t v = stream_load16<NT>(p + 64 * i);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) rw.k[u][4 * i + w] = v[w];
+        }
+        if constexpr (KV == kMXFP4) {
+          rw.ks[u] = stream_load1<NT>(ksdata + pt * SROW + g);
+          int64_t tv = base + 16 * u + lane / 4;
+          tv = tv < last ? tv : last;
+          rw.vs[u] = stream_load1<NT>(vsdata + hrow(tv) * SROW + (lane & 3));
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
         int64_t t = base + 16 * (e / 4) + (e % 4) + 4 * g;
         t = t < last ? t : last;
-        p = vdata + hrow(t) * ROW + Lay::kVBytes * r16;
-      }
-      if constexpr (Lay::kVBytes == 16) {
-        const u32x4_t v = stream_load16<NT>(p);
-        rw.v[e][0] = v[0];
-        rw.v[e][1] = v[1];
-        rw.v[e][2] = v[2];
-        rw.v[e][3] = v[3];
-      } else if constexpr (Lay::kVBytes == 8) {
-        const u32x2_t v = stream_load8<NT>(p);
-        rw.v[e][0] = v[0];
-        rw.v[e][1] = v[1];
-      } else {
-        rw.v[e][0] = stream_load4<NT>(p);
+        const uint8_t* p = vdata + hrow(t) * ROW + Lay::kVBytes * r16;
+        if constexpr (Lay::kVBytes == 16) {
+          const u32x4_t v = stream_load16<NT>(p);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) rw.v[e][w] = v[w];
+        } else if constexpr (Lay::kVBytes == 8) {
+          const u32x2_t v = stream_load8<NT>(p);
+          rw.v[e][0] = v[0];
+          rw.v[e][1] = v[1];
+        } else {
+          rw.v[e][0] = stream_load4<NT>(p);
+        }
       }
     }
   };
@@ -521,12 +548,15 @@ void gqa_mfma_kernel(PartialArgs a) {
       for (int e = 0; e < 4; ++e) x[4 * u + e] = s[e];
     }
   };
-  // Tile max of the lane's head in the log2 domain.
-  auto tile_max2 = [&](const float (&x)[8]) {
+  // Max of the lane's 8 logits of its head, in the log2 domain.  Whether the
+  // running max must move is decided on these lane maxima (any lane over its
+  // head's max + 2^kLazyMax); only then is the head's tile max reduced over
+  // its 4 lane groups, so all 4 keep the same running max.
+  auto lane_max2 = [&](const float (&x)[8]) {
     float tmax = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-    return rows4_max(tmax) * c2;
+    return tmax * c2;
   };
   // Move the running max to mn, rescaling the state.
   auto rescale = [&](float& m, float& l, f32x4_t (&o)[8], float mn) {
@@ -578,8 +608,8 @@ void gqa_mfma_kernel(PartialArgs a) {
         for (int i = 0; i < 4; ++i)
           if (16 * u + 4 * g + i >= nvalid) x[4 * u + i] = -INFINITY;
     }
-    const float tmax2 = tile_max2(x);
-    if (__any(tmax2 > m + kLazyMax)) rescale(m, l, o, fmaxf(m, tmax2));
+    const float lmax2 = lane_max2(x);
+    if (__any(lmax2 > m + kLazyMax)) rescale(m, l, o, fmaxf(m, rows4_max(lmax2)));
     bf16x8_t pop, pol;
     weights(x, m, l, pop, pol, mask_tag);
     // one MFMA pair per 16-column block
@@ -620,17 +650,19 @@ void gqa_mfma_kernel(PartialArgs a) {
           for (int e = 0; e < 4; ++e)
             if (16 * u + 4 * g + e >= nv[i]) x[i][4 * u + e] = -INFINITY;
     }
-    float tmax2[TW];
+    float lmax2[TW];
     bool need = false;
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-      tmax2[i] = tile_max2(x[i]);
-      need = need || (tmax2[i] > m2[i] + kLazyMax);
+      lmax2[i] = lane_max2(x[i]);
+      need = need || (lmax2[i] > m2[i] + kLazyMax);
     }
     if (__any(need)) {
 #pragma unroll
-      for (int i = 0; i < TW; ++i)
-        if (__any(tmax2[i] > m2[i] + kLazyMax)) rescale(m2[i], lsum[i], acc[i], fmaxf(m2[i], tmax2[i]));
+      for (int i = 0; i < TW; ++i) {
+        const float tmax2 = rows4_max(lmax2[i]);
+        if (__any(tmax2 > m2[i] + kLazyMax)) rescale(m2[i], lsum[i], acc[i], fmaxf(m2[i], tmax2));
+      }
     }
     bf16x8_t pop[TW], pol[TW];
 #pragma unroll
