@@ -161,6 +161,31 @@ typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
+// Longest-request-first order of the shard units.  Position p of the unit
+// queue (workgroups start roughly in id order) takes a unit of the request
+// ranked p / (kvp Hkv) by sequence length, longest first (ties by index), so
+// the longest shards start first and the short ones fill the tail of the
+// grid.  Lane b of the wave holds request b's length and counts the requests
+// ahead of it; up to 64 requests, larger batches keep the plain order.
+// Every unit keeps its (shard, KV head) and every request keeps its units, so
+// this only permutes which workgroup does which unit.
+__device__ __forceinline__ int64_t longest_first_unit(int64_t p, const PartialArgs& a) {
+  if (a.B <= 1 || a.B > 64) return p;
+  const int per = a.kvp * a.Hkv;
+  const int r = (int)(p / per);
+  const int rem = (int)(p - (int64_t)r * per);
+  const int lane = threadIdx.x & 63;
+  const int my = lane < a.B ? a.seq_lens[lane] : -1;
+  int ahead = 0;
+  for (int b2 = 0; b2 < a.B; ++b2) {
+    const int o = __builtin_amdgcn_readlane(my, b2);
+    ahead += (o > my || (o == my && b2 < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __ballot(lane < a.B && ahead == r);
+  const int b = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+  return ((int64_t)(rem / a.Hkv) * a.B + b) * a.Hkv + rem % a.Hkv;
+}
+
 // LDS of the final merge of the four waves' states.
 struct MergeLds {
   float o[kWaves][16][kD + 4];
@@ -350,6 +375,7 @@ void gqa_mfma_kernel(PartialArgs a) {
   int64_t unit;
   int chunk;
   if (!unit_token(blockIdx.x, (int64_t)a.kvp * a.B * a.Hkv, nchunks, &unit, &chunk)) return;
+  unit = longest_first_unit(unit, a);
   const int kvh = (int)(unit % a.Hkv);
   const int b = (int)(unit / a.Hkv % a.B);
   const int j = (int)(unit / ((int64_t)a.Hkv * a.B));
