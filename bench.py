@@ -38,12 +38,12 @@ METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S
 # counters were taken on).  Changed kernel code no longer matches, and the
 # bench then reports traffic as null.  Summaries are under profiles/.
 TRAFFIC = {
-    ("helix_fp8", "contiguous", 32, 1, "93716dbee1785208"): 17331953893,
-    ("helix_fp8", "paged16", 32, 1, "93716dbee1785208"): 17351505815,
-    ("helix_fp8", "contiguous", 32, 4, "93716dbee1785208"): 17850541888,
-    ("helix_mxfp4", "contiguous", 32, 1, "93716dbee1785208"): 9231652589,
-    ("gqa_bf16_varlen", "contiguous", 16, 1, "93716dbee1785208"): 3480055547,
-    ("gqa_bf16_varlen", "contiguous", 16, 4, "93716dbee1785208"): 3475531438,
+    ("helix_fp8", "contiguous", 32, 1, "d69d0dbba97f3aad"): 17330191722,
+    ("helix_fp8", "paged16", 32, 1, "d69d0dbba97f3aad"): 17353751486,
+    ("helix_fp8", "contiguous", 32, 4, "d69d0dbba97f3aad"): 18260254060,
+    ("helix_mxfp4", "contiguous", 32, 1, "d69d0dbba97f3aad"): 9249447965,
+    ("gqa_bf16_varlen", "contiguous", 16, 1, "d69d0dbba97f3aad"): 3482797848,
+    ("gqa_bf16_varlen", "contiguous", 16, 4, "d69d0dbba97f3aad"): 3464823378,
     ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 4901559411,
 }
 # Fraction of the partial kernel's SIMD cycles with the matrix cores busy,
@@ -51,8 +51,8 @@ TRAFFIC = {
 # rocprofv3 --pmc run; same keys as TRAFFIC.
 MFMA_BUSY = {
     ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 0.5503,
-    ("helix_mxfp4", "contiguous", 32, 1, "93716dbee1785208"): 0.3393,
-    ("helix_fp8", "contiguous", 32, 1, "93716dbee1785208"): 0.1722,
+    ("helix_mxfp4", "contiguous", 32, 1, "d69d0dbba97f3aad"): 0.3408,
+    ("helix_fp8", "contiguous", 32, 1, "d69d0dbba97f3aad"): 0.1656,
 }
 KERNEL_SOURCES = {"bf16": "partial_gqa_mfma.hip", "fp8": "partial_gqa_mfma.hip",
                   "mxfp4": "partial_gqa_mfma.hip", "f32": "partial_valu.hip"}

@@ -166,9 +166,10 @@ typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 // ranked p / (kvp Hkv) by sequence length, longest first (ties by index), so
 // the longest shards start first and the short ones fill the tail of the
 // grid.  Lane b of the wave holds request b's length and counts the requests
-// ahead of it; up to 64 requests, larger batches keep the plain order.
-// Every unit keeps its (shard, KV head) and every request keeps its units, so
-// this only permutes which workgroup does which unit.
+// ahead of it; up to 64 requests.  Larger batches, and batches whose requests
+// all have one length, keep the plain (shard-major) order.  Every unit keeps
+// its (shard, KV head) and every request keeps its units, so this only
+// permutes which workgroup does which unit.
 __device__ __forceinline__ int64_t longest_first_unit(int64_t p, const PartialArgs& a) {
   if (a.B <= 1 || a.B > 64) return p;
   const int per = a.kvp * a.Hkv;
@@ -176,6 +177,7 @@ __device__ __forceinline__ int64_t longest_first_unit(int64_t p, const PartialAr
   const int rem = (int)(p - (int64_t)r * per);
   const int lane = threadIdx.x & 63;
   const int my = lane < a.B ? a.seq_lens[lane] : -1;
+  if (__ballot(lane < a.B && my != __builtin_amdgcn_readfirstlane(my)) == 0) return p;
   int ahead = 0;
   for (int b2 = 0; b2 < a.B; ++b2) {
     const int o = __builtin_amdgcn_readlane(my, b2);
