@@ -338,9 +338,10 @@ __device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_la
 }
 
 // PAGED: rows are found through the block table (paged cache layout).
-// NT: cache loads carry the non-temporal hint (one query token: every byte is
-// read once); several query tokens read each byte once per token chunk, from
-// the caches when the loads are plain.
+// NT: cache loads carry the non-temporal hint: every cache byte is read once
+// when one token chunk covers all query tokens.  With several chunks each
+// chunk reads the shard's rows, the loads are plain, and the later chunks of
+// a shard find them in the caches.
 // TW: query tokens per workgroup.  Each wave decodes a tile once and runs the
 // logits, softmax and PV product of each of the TW tokens on it; every token
 // keeps its own Q operands, softmax state and accumulator.
@@ -964,25 +965,40 @@ int tokens_per_workgroup(int T, int kv) {
   return (kv == kBF16 && T >= 3) ? 4 : 2;
 }
 
+// The four-token instance (bf16 cache, LDS ring of tiles) with NT loads or not.
+template <int KV, bool PAGED, bool NT>
+hipError_t launch_gqa_ring(const PartialArgs& a, dim3 grid, hipStream_t stream) {
+  constexpr size_t kLds = (size_t)kWaves * Ring::kWaveBytes;
+  static_assert(kLds >= sizeof(MergeLds) && kLds <= 160 * 1024, "LDS ring budget");
+  auto fn = gqa_mfma_kernel<KV, PAGED, NT, 4, true>;
+  // more than 64 KB of dynamic LDS: raise the kernel's limit once (the
+  // initialization of a local static is thread-safe)
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(fn, grid, dim3(kThreads), kLds, stream, a);
+  return hipSuccess;
+}
+
+// When one token chunk covers all T tokens every cache byte is read once, so
+// the loads carry the non-temporal hint as for a single token; with several
+// chunks they are plain, and the later chunks of a shard find its rows in L2.
 template <int KV, bool PAGED>
 hipError_t launch_gqa3(const PartialArgs& a, hipStream_t stream) {
   const int tw = tokens_per_workgroup(a.T, KV);
-  const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, (a.T + tw - 1) / tw);
+  const int nchunks = (a.T + tw - 1) / tw;
+  const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, nchunks);
   const dim3 grid((unsigned)blocks), block(kThreads);
   if (tw == 1) {
     hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, true, 1, false>), grid, block, 0, stream, a);
   } else if (tw == 2) {
-    hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, false, 2, false>), grid, block, 0, stream, a);
+    if (nchunks == 1)
+      hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, true, 2, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, false, 2, false>), grid, block, 0, stream, a);
   } else if constexpr (KV == kBF16) {
-    constexpr size_t kLds = (size_t)kWaves * Ring::kWaveBytes;
-    static_assert(kLds >= sizeof(MergeLds) && kLds <= 160 * 1024, "LDS ring budget");
-    auto fn = gqa_mfma_kernel<KV, PAGED, false, 4, true>;
-    // more than 64 KB of dynamic LDS: raise the kernel's limit once (the
-    // initialization of a local static is thread-safe)
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(fn, grid, block, kLds, stream, a);
+    return nchunks == 1 ? launch_gqa_ring<KV, PAGED, true>(a, grid, stream)
+                        : launch_gqa_ring<KV, PAGED, false>(a, grid, stream);
   } else {
     return hipErrorInvalidValue;   // no four-token instance for this format
   }

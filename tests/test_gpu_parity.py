@@ -159,6 +159,22 @@ def test_rising_logits(kind):
         gc.compare(o, lse, ref_o, ref_l, w.kv_dtype, "%s ramp kvp=%d merged" % (kind, kvp))
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_many_requests_mixed_lengths(B):
+    """Up to 64 requests the shard units are taken longest request first
+    (ranked on the device, one lane per request); from 65 on in plain order.
+    Both must give every request's exact partials, including repeated and
+    zero lengths."""
+    import numpy as np
+    rng = np.random.default_rng(B)
+    lens = [int(x) for x in rng.integers(0, 120, B)]
+    lens[3] = lens[5] = 77          # ties
+    lens[7] = 0                     # empty request
+    w = W("many_%d" % B, B=B, Hq=16, Hkv=1, S_max=120, seq_lens=tuple(lens), kv_dtype="fp8", seed=B)
+    for kvp in (1, 3):
+        gc.check_full(w, kvp)
+
+
 @pytest.mark.parametrize("kv", ["fp8", "mxfp4"])
 def test_query_dynamic_range(kv):
     """Queries far from N(0, 1): per-head magnitudes from 2^-40 to 2^4, elements
