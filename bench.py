@@ -38,12 +38,12 @@ METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S
 # counters were taken on).  Changed kernel code no longer matches, and the
 # bench then reports traffic as null.  Summaries are under profiles/.
 TRAFFIC = {
-    ("helix_fp8", "contiguous", 32, 1, "d69d0dbba97f3aad"): 17330191722,
-    ("helix_fp8", "paged16", 32, 1, "d69d0dbba97f3aad"): 17353751486,
-    ("helix_fp8", "contiguous", 32, 4, "d69d0dbba97f3aad"): 18260254060,
-    ("helix_mxfp4", "contiguous", 32, 1, "d69d0dbba97f3aad"): 9249447965,
-    ("gqa_bf16_varlen", "contiguous", 16, 1, "d69d0dbba97f3aad"): 3482797848,
-    ("gqa_bf16_varlen", "contiguous", 16, 4, "d69d0dbba97f3aad"): 3464823378,
+    ("helix_fp8", "contiguous", 32, 1, "c31dcba5ec5200a5"): 17321408531,
+    ("helix_fp8", "paged16", 32, 1, "c31dcba5ec5200a5"): 17365359462,
+    ("helix_fp8", "contiguous", 32, 4, "c31dcba5ec5200a5"): 18740136748,
+    ("helix_mxfp4", "contiguous", 32, 1, "c31dcba5ec5200a5"): 9240803942,
+    ("gqa_bf16_varlen", "contiguous", 16, 1, "c31dcba5ec5200a5"): 3483218690,
+    ("gqa_bf16_varlen", "contiguous", 16, 4, "c31dcba5ec5200a5"): 3487265176,
     ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 4901559411,
 }
 # Fraction of the partial kernel's SIMD cycles with the matrix cores busy,
@@ -51,8 +51,8 @@ TRAFFIC = {
 # rocprofv3 --pmc run; same keys as TRAFFIC.
 MFMA_BUSY = {
     ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 0.5503,
-    ("helix_mxfp4", "contiguous", 32, 1, "d69d0dbba97f3aad"): 0.3408,
-    ("helix_fp8", "contiguous", 32, 1, "d69d0dbba97f3aad"): 0.1656,
+    ("helix_mxfp4", "contiguous", 32, 1, "c31dcba5ec5200a5"): 0.3529,
+    ("helix_fp8", "contiguous", 32, 1, "c31dcba5ec5200a5"): 0.1797,
 }
 KERNEL_SOURCES = {"bf16": "partial_gqa_mfma.hip", "fp8": "partial_gqa_mfma.hip",
                   "mxfp4": "partial_gqa_mfma.hip", "f32": "partial_valu.hip"}
