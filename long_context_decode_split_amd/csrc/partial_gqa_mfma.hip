@@ -342,9 +342,9 @@ __device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_la
 // when one token chunk covers all query tokens.  With several chunks each
 // chunk reads the shard's rows, the loads are plain, and the later chunks of
 // a shard find them in the caches.
-// TW: query tokens per workgroup.  Each wave decodes a tile once and runs the
-// logits, softmax and PV product of each of the TW tokens on it; every token
-// keeps its own Q operands, softmax state and accumulator.
+// TW: query tokens per workgroup.  Each wave loads a tile (and decodes its V)
+// once and runs the logits, softmax and PV product of each of the TW tokens on
+// it; every token keeps its own Q operands, softmax state and accumulator.
 // LDSRING: the tiles ahead wait in an LDS ring filled by direct-to-LDS loads
 // (Ring, bf16 cache) instead of in registers, which leaves the registers to the
 // tokens and keeps several tiles in flight at one wave per SIMD.
@@ -707,8 +707,12 @@ void gqa_mfma_kernel(PartialArgs a) {
 
   // MASK: the tile runs past the shard end (single token: its extra tokens get
   // zero weight).  With several tokens every token checks its own cut.
-  using Full = std::true_type;
-  using Part = std::false_type;
+  using Masked = std::true_type;      // compute: rows past a token's cut get weight 0
+  using Unmasked = std::false_type;
+  using FullTile = std::true_type;    // load: every row of the tile inside the shard
+  using PartTile = std::false_type;
+  using Clamped = std::true_type;     // issue: rows clamped to the shard, lane by lane
+  using Unclamped = std::false_type;
   auto compute = [&](const Raw<KV>& rw, int tile, auto mask_tag) {
     const int64_t base = s0 + (int64_t)tile * kTile;
     if constexpr (TW == 1) {
@@ -722,9 +726,9 @@ void gqa_mfma_kernel(PartialArgs a) {
         nv[i] = n < 0 ? 0 : (n > kTile ? kTile : (int)n);
       }
       if (nv[0] == kTile)                        // every token sees the whole tile
-        tokens_tile(rw, nv, Part{});
+        tokens_tile(rw, nv, Unmasked{});
       else
-        tokens_tile(rw, nv, Full{});
+        tokens_tile(rw, nv, Masked{});
     }
   };
 
@@ -798,28 +802,28 @@ void gqa_mfma_kernel(PartialArgs a) {
     if (nfull > 0) {
       auto clampt = [&](int t) { return t < nfull - 1 ? t : nfull - 1; };
 #pragma unroll
-      for (int k = 0; k < R::kSlots - 1; ++k) issue(clampt(wave + k * kWaves), k, Part{});
+      for (int k = 0; k < R::kSlots - 1; ++k) issue(clampt(wave + k * kWaves), k, Unclamped{});
       int sl = 0;
       for (int tile = wave; tile < nfull; tile += kWaves) {
         // refill the slot read in the previous iteration, kSlots - 1 tiles ahead
-        issue(clampt(tile + (R::kSlots - 1) * kWaves), sl == 0 ? R::kSlots - 1 : sl - 1, Part{});
+        issue(clampt(tile + (R::kSlots - 1) * kWaves), sl == 0 ? R::kSlots - 1 : sl - 1, Unclamped{});
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((R::kSlots - 1) * R::kDmaPerTile));
         asm volatile("" ::: "memory");
         Raw<KV> rw;
         fetch(rw, sl);
-        compute(rw, tile, Part{});
+        compute(rw, tile, Unmasked{});
         sl = sl + 1 == R::kSlots ? 0 : sl + 1;
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       asm volatile("" ::: "memory");
     }
     if (nfull < ntiles && nfull % kWaves == wave) {
-      issue(nfull, 0, Full{});
+      issue(nfull, 0, Clamped{});
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       asm volatile("" ::: "memory");
       Raw<KV> rt;
       fetch(rt, 0);
-      compute(rt, nfull, Full{});
+      compute(rt, nfull, Masked{});
     }
     __syncthreads();   // every wave is done with its slots before the merge reuses them
   } else {
@@ -834,62 +838,40 @@ void gqa_mfma_kernel(PartialArgs a) {
       int tile = wave;
       if constexpr (kRing == 2) {
         Raw<KV> ra, rb;
-        load(ra, clampt(tile), Full{});
+        load(ra, clampt(tile), FullTile{});
         while (tile < nfull) {
-          load(rb, clampt(tile + kWaves), Full{});
-          compute(ra, tile, Part{});
+          load(rb, clampt(tile + kWaves), FullTile{});
+          compute(ra, tile, Unmasked{});
           tile += kWaves;
           if (tile >= nfull) break;
-          load(ra, clampt(tile + kWaves), Full{});
-          compute(rb, tile, Part{});
-          tile += kWaves;
-        }
-      } else if constexpr (kRing == 3) {
-        Raw<KV> ra, rb, rc;
-        load(ra, clampt(tile), Full{});
-        load(rb, clampt(tile + kWaves), Full{});
-        while (tile < nfull) {
-          load(rc, clampt(tile + 2 * kWaves), Full{});
-          compute(ra, tile, Part{});
-          tile += kWaves;
-          if (tile >= nfull) break;
-          load(ra, clampt(tile + 2 * kWaves), Full{});
-          compute(rb, tile, Part{});
-          tile += kWaves;
-          if (tile >= nfull) break;
-          load(rb, clampt(tile + 2 * kWaves), Full{});
-          compute(rc, tile, Part{});
+          load(ra, clampt(tile + kWaves), FullTile{});
+          compute(rb, tile, Unmasked{});
           tile += kWaves;
         }
       } else {
-        static_assert(kRing == 4, "ring of 2, 3 or 4 buffers");
-        Raw<KV> ra, rb, rc, rd;
-        load(ra, clampt(tile), Full{});
-        load(rb, clampt(tile + kWaves), Full{});
-        load(rc, clampt(tile + 2 * kWaves), Full{});
+        static_assert(kRing == 3, "ring of 2 or 3 buffers");
+        Raw<KV> ra, rb, rc;
+        load(ra, clampt(tile), FullTile{});
+        load(rb, clampt(tile + kWaves), FullTile{});
         while (tile < nfull) {
-          load(rd, clampt(tile + 3 * kWaves), Full{});
-          compute(ra, tile, Part{});
+          load(rc, clampt(tile + 2 * kWaves), FullTile{});
+          compute(ra, tile, Unmasked{});
           tile += kWaves;
           if (tile >= nfull) break;
-          load(ra, clampt(tile + 3 * kWaves), Full{});
-          compute(rb, tile, Part{});
+          load(ra, clampt(tile + 2 * kWaves), FullTile{});
+          compute(rb, tile, Unmasked{});
           tile += kWaves;
           if (tile >= nfull) break;
-          load(rb, clampt(tile + 3 * kWaves), Full{});
-          compute(rc, tile, Part{});
-          tile += kWaves;
-          if (tile >= nfull) break;
-          load(rc, clampt(tile + 3 * kWaves), Full{});
-          compute(rd, tile, Part{});
+          load(rb, clampt(tile + 2 * kWaves), FullTile{});
+          compute(rc, tile, Unmasked{});
           tile += kWaves;
         }
       }
     }
     if (nfull < ntiles && nfull % kWaves == wave) {
       Raw<KV> rt;
-      load(rt, nfull, Part{});
-      compute(rt, nfull, Full{});
+      load(rt, nfull, PartTile{});
+      compute(rt, nfull, Masked{});
     }
   }
   // ---- merge the four waves' states of each token and write its partial
