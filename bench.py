@@ -38,12 +38,12 @@ METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S
 # counters were taken on).  Changed kernel code no longer matches, and the
 # bench then reports traffic as null.  Summaries are under profiles/.
 TRAFFIC = {
-    ("helix_fp8", "contiguous", 32, 1, "c31dcba5ec5200a5"): 17321408531,
-    ("helix_fp8", "paged16", 32, 1, "c31dcba5ec5200a5"): 17365359462,
-    ("helix_fp8", "contiguous", 32, 4, "c31dcba5ec5200a5"): 18740136748,
-    ("helix_mxfp4", "contiguous", 32, 1, "c31dcba5ec5200a5"): 9240803942,
-    ("gqa_bf16_varlen", "contiguous", 16, 1, "c31dcba5ec5200a5"): 3483218690,
-    ("gqa_bf16_varlen", "contiguous", 16, 4, "c31dcba5ec5200a5"): 3487265176,
+    ("helix_fp8", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 17328989465,
+    ("helix_fp8", "paged16", 32, 1, "f0510cf1dd96ce3c"): 17350776854,
+    ("helix_fp8", "contiguous", 32, 4, "f0510cf1dd96ce3c"): 18638267018,
+    ("helix_mxfp4", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 9230341008,
+    ("gqa_bf16_varlen", "contiguous", 16, 1, "f0510cf1dd96ce3c"): 3482922455,
+    ("gqa_bf16_varlen", "contiguous", 16, 4, "f0510cf1dd96ce3c"): 3487459233,
     ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 4901559411,
 }
 # Fraction of the partial kernel's SIMD cycles with the matrix cores busy,
@@ -51,8 +51,8 @@ TRAFFIC = {
 # rocprofv3 --pmc run; same keys as TRAFFIC.
 MFMA_BUSY = {
     ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 0.5503,
-    ("helix_mxfp4", "contiguous", 32, 1, "c31dcba5ec5200a5"): 0.3529,
-    ("helix_fp8", "contiguous", 32, 1, "c31dcba5ec5200a5"): 0.1797,
+    ("helix_mxfp4", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 0.3513,
+    ("helix_fp8", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 0.1730,
 }
 KERNEL_SOURCES = {"bf16": "partial_gqa_mfma.hip", "fp8": "partial_gqa_mfma.hip",
                   "mxfp4": "partial_gqa_mfma.hip", "f32": "partial_valu.hip"}
