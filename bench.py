@@ -165,8 +165,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU's share of the split-KV path; runs on more than one GPU "
-              "are not part of this build (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU's share of the split-KV path; the library runs on one GPU "
+              "and has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -59,7 +59,7 @@
  *    aligned; seq_lens, lse, lse_part and scale pointers 4-byte aligned.
  *  - Errors: every argument is validated on the host before anything is
  *    enqueued; an invalid call returns KVD_ERR_INVALID (malformed) or
- *    KVD_ERR_UNSUPPORTED (well formed, but no kernel of this build handles it)
+ *    KVD_ERR_UNSUPPORTED (well formed, but no kernel of the library handles it)
  *    and enqueues nothing.  A launch failure reported by the HIP runtime
  *    returns KVD_ERR_HIP.  kvd_last_error() gives the calling thread's message
  *    for its last failed call.
