@@ -380,7 +380,7 @@ def main():
         # latent heads run on bf16 MFMA: report the matrix-core share of the
         # partial pass.  The product P.V runs twice (P as a bf16 hi + lo pair),
         # so the executed MFMA flops exceed the algorithmic ones.
-        executed = roofline.attention_flops(w.Hq, seq, w.Dqk, 2 * w.Dv)
+        executed = roofline.attention_flops_tokens(w.Hq, seq, T, w.Dqk, 2 * w.Dv)
         t = partial_avg * 1e-3
         res["roofline"]["mfma"] = {
             "busy_frac_counter": MFMA_BUSY.get((w.name, lay_key, kvp, T, khash)),
