@@ -129,6 +129,17 @@ def test_token_counts_ring_formats(kv):
         _check(w, T, "contiguous", kvp, S, [(S, 77), (19, S - 1)], seed=11)
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("kv,T", [("fp8", 2), ("mxfp4", 2), ("bf16", 2), ("bf16", 4)])
+def test_one_chunk_token_counts(layout, kv, T):
+    """Token counts that one workgroup chunk covers (two tokens; four on the
+    bf16 ring): those instances read the cache with non-temporal loads."""
+    kvp = 3
+    S = 192
+    w = _wl(kv, S=S, Hq=32, Hkv=2, D=128)
+    _check(w, T, layout, kvp, S, [(S * kvp, 70), (T, 1)], seed=12 + T)
+
+
 def test_mla_multi_token_paged():
     kvp, T, S = 5, 3, 192
     w = _wl("bf16", S=S, **SHAPES["mla"])
