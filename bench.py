@@ -134,59 +134,41 @@ def cpu_baseline(w, target_s=15.0):
             "seconds": elapsed, "bytes": int(done_bytes)}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed steps first: the clocks settle over the first few dozen launches")
-    ap.add_argument("--workload", default="helix_fp8")
-    ap.add_argument("--kvp", type=int, default=None)
-    ap.add_argument("--layout", default="contiguous", choices=["contiguous", "striped", "staggered16", "paged"],
-                    help="cache layout; a sharded layout views the generated cache as kvp shards of "
-                         "S/kvp rows, the paged layout as a pool of blocks handed to the requests in "
-                         "a seeded random order (same bytes, same per-step traffic)")
-    ap.add_argument("--block-len", type=int, default=16, help="tokens per block of the paged layout")
-    ap.add_argument("--q-tokens", type=int, default=1,
-                    help="query tokens per request (a multi-token turn, causal among the new tokens; "
-                         "the cache's last T tokens are the new ones)")
-    ap.add_argument("--no-append", action="store_true", help="skip timing kvd_append_kv")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step (partial pass + merge) captured once into a HIP graph "
-                         "and replayed; reported under 'graph'")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time steps that each start with the last-level cache flushed "
-                         "(for workloads whose cache fits in it); reported under 'cold'")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device-to-device copy of BYTES, 5 times (the "
-                         "reference kernel for scaling HBM byte counters), and exit")
-    args = ap.parse_args()
+# How each kernel family computes, for the bench line (keyed by kv format;
+# "latent" for the 576/512 latent-head kernel).
+ARITH = {
+    "f32": "fp32 vector ALU: logits, softmax and P.V in fp32",
+    "bf16": "bf16 MFMA logits (16x16x32) on the bf16 cache; P.V on bf16 MFMA with P as a bf16 hi+lo pair; "
+            "fp32 accumulation and softmax",
+    "fp8": "block-scaled f8f6f4 MFMA logits on the raw E4M3 K bytes with the bf16 query as two E4M3 parts "
+           "(unit block scales, the fp32 slab scale folded into the log2 multiplier); V decoded to bf16, P.V on "
+           "bf16 MFMA with P as a bf16 hi+lo pair; fp32 accumulation and softmax",
+    "mxfp4": "block-scaled f8f6f4 MFMA logits on the raw E2M1 K nibbles with their E8M0 block exponents and the "
+             "bf16 query as two E4M3 parts; V decoded to bf16 with its block scales, P.V on bf16 MFMA with P as a "
+             "bf16 hi+lo pair; fp32 accumulation and softmax",
+    "latent": "bf16 MFMA logits over the 576-wide latent rows and P.V over their first 512 columns (P as a bf16 "
+              "hi+lo pair), tiles staged through an LDS ring; fp32 accumulation and softmax",
+}
+# Executed P.V flops per algorithmic ones on the latent kernel (P as a bf16
+# hi+lo pair runs the product twice).
+LATENT_PV_PASSES = 2
 
-    if args.gpus != 1:
-        print("bench.py measures one GPU's share of the split-KV path; the library runs on one GPU "
-              "and has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+# Workloads measured next to the headline by a default run (the MXFP4 Helix
+# shape and the latent-head shape, both at kvp = 32).
+EXTRA = (("helix_mxfp4", 32), ("mla_bf16", 32))
 
+
+def measure(args, name, kvp_req, T, layout, block_len, timing_extras=True):
+    """One workload: generate it into device memory, time `args.steps` steps
+    after `args.warmup`, and return the result fields (no cpu_baseline)."""
     import torch
-
-    if args.copy_calibration:
-        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": args.copy_calibration, "launches": 5}))
-        return
 
     import kvgen
     from kvgen.device import generate_on_device
     from long_context_decode_split_amd import kvd, roofline
 
-    T = args.q_tokens
-    w = kvgen.WORKLOADS[args.workload].with_(q_tokens=T)
-    kvp = args.kvp or (32 if 32 in w.kvp else w.kvp[0])
+    w = kvgen.WORKLOADS[name].with_(q_tokens=T)
+    kvp = kvp_req or (32 if 32 in w.kvp else w.kvp[0])
     torch.cuda.set_device(0)
     log("generating %s (kvp=%d) into device memory" % (w.name, kvp))
     t0 = time.time()
@@ -195,8 +177,8 @@ def main():
 
     S_cache = w.S_max
     paging = {}
-    if args.layout == "paged":
-        bl = args.block_len
+    if layout == "paged":
+        bl = block_len
         if w.S_max % bl:
             raise SystemExit("S_max %d is not a multiple of block_len %d" % (w.S_max, bl))
         max_blocks = w.S_max // bl
@@ -212,7 +194,7 @@ def main():
         gen = torch.Generator().manual_seed(1234)
         table = torch.randperm(num_blocks, generator=gen).to(torch.int32).view(w.B, max_blocks).cuda()
         paging = dict(block_len=bl, max_blocks=max_blocks, num_blocks=num_blocks, block_table=table)
-    elif args.layout != "contiguous":
+    elif layout != "contiguous":
         # the same generated bytes viewed as kvp shards of S/kvp rows each
         if w.S_max % kvp:
             raise SystemExit("S_max %d is not a multiple of kvp %d" % (w.S_max, kvp))
@@ -228,7 +210,7 @@ def main():
         if dev.v is not None:
             dev.v = (shard_view(dev.v[0], True), shard_view(dev.v[1], mx))
     p = kvd.problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, S_cache, kvp, w.q_dtype, w.kv_dtype, 0.0, w.v_aliases_k,
-                    layout=args.layout, q_tokens=T, **paging)
+                    layout=layout, q_tokens=T, **paging)
     f32 = dict(dtype=torch.float32, device="cuda")
     o_part = torch.empty((kvp, w.B, T, w.Hq, w.Dv), **f32)
     lse_part = torch.empty((kvp, w.B, T, w.Hq), **f32)
@@ -270,34 +252,27 @@ def main():
     partial_avg = sum(partial_ms) / len(partial_ms)
     step_ms = [a_ + b_ for a_, b_ in zip(partial_ms, merge_ms)]
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
+    log("%s kvp=%d T=%d: partial %.1f us, step %.1f us" % (w.name, kvp, T, partial_avg * 1e3, ms_per_step * 1e3))
 
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (partial_avg * 1e-3) / 1e9
     peak = roofline.HBM_BYTES_PER_S / 1e9
     khash = kernel_hash(w.kv_dtype, mla=w.v_aliases_k)
-    lay_key = args.layout + (str(args.block_len) if args.layout == "paged" else "")
+    lay_key = layout + (str(block_len) if layout == "paged" else "")
     traffic = TRAFFIC.get((w.name, lay_key, kvp, T, khash))
+    fam = "latent" if w.v_aliases_k else w.kv_dtype
     res = {
-        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "hbm_peak_frac": round(value / peak, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32" if w.kv_dtype == "f32" else "bf16",
-        "arith": "f32 vector ALU" if w.kv_dtype == "f32" else
-                 "bf16 MFMA on exactly decoded %s cache, fp32 accumulate and softmax" % w.kv_dtype,
-        "data": "synthetic (seeded N(0,1), encoded to the cache format)",
-        "config": {"workload": w.name, "layout": args.layout,
-                   "block_len": args.block_len if args.layout == "paged" else None, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Hsz": w.Dqk, "Dv": w.Dv,
-                   "S": w.S_max, "kvp": kvp, "q_tokens": T, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
-                   "kv_bytes": kv_bytes, "flops": flops},
+        "dtype": w.kv_dtype,
+        "arith": ARITH[fam],
+        "config": {"workload": w.name, "layout": layout,
+                   "block_len": block_len if layout == "paged" else None, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Hsz": w.Dqk, "Dv": w.Dv, "S": w.S_max, "kvp": kvp, "q_tokens": T, "kv_dtype": w.kv_dtype,
+                   "q_dtype": w.q_dtype, "kv_bytes": kv_bytes, "flops": flops},
         "partial_us": round(partial_avg * 1e3, 2),
         "partial_us_median": round(median(partial_ms) * 1e3, 2),
         "partial_us_min": round(min(partial_ms) * 1e3, 2),
@@ -318,7 +293,20 @@ def main():
         res["roofline"].update({"bound": "alu" if w.kv_dtype == "f32" else "mfma", "achieved": round(ach, 2),
                                 "peak": fpeak / 1e12, "unit": "TFLOP/s", "frac": round(ach / (fpeak / 1e12), 4),
                                 "flops_per_launch": flops, "hbm_frac": round(achieved / peak, 4)})
-    if not args.no_append:
+    if w.v_aliases_k:
+        # latent heads run on bf16 MFMA: report the matrix-core share of the
+        # partial pass, algorithmic and as executed
+        executed = roofline.attention_flops_tokens(w.Hq, seq, T, w.Dqk, LATENT_PV_PASSES * w.Dv)
+        t = partial_avg * 1e-3
+        res["roofline"]["mfma"] = {
+            "busy_frac_counter": MFMA_BUSY.get((w.name, lay_key, kvp, T, khash)),
+            "peak_tflops": roofline.MFMA_BF16_FLOPS / 1e12,
+            "algorithmic_tflops": round(flops / t / 1e12, 2),
+            "algorithmic_frac": round(flops / t / roofline.MFMA_BF16_FLOPS, 4),
+            "executed_tflops": round(executed / t / 1e12, 2),
+            "executed_frac": round(executed / t / roofline.MFMA_BF16_FLOPS, 4),
+            "executed_flops": executed}
+    if timing_extras and not args.no_append:
         # one step's KV write: T new fp32 token rows per (request, KV head),
         # appended at the last T positions of every request
         kn = torch.randn((w.B, T, w.Hkv, w.Dqk), dtype=torch.float32, device="cuda")
@@ -335,7 +323,7 @@ def main():
                 if i >= args.warmup:
                     app.append(e[0].elapsed_time(e[1]))
         res["append_us_median"] = round(median(app) * 1e3, 2)
-    if args.graph:
+    if timing_extras and args.graph:
         # The same step captured once and replayed: launch overhead leaves the
         # timed region (it matters for the small, latency-bound workloads).
         g = torch.cuda.CUDAGraph()
@@ -356,7 +344,7 @@ def main():
         res["graph"] = {"us_per_step": round(g_ms * 1e3, 2), "value": round(kv_bytes / (g_ms * 1e-3) / 1e9, 2),
                         "unit": "GB/s", "note": "the step replayed from a HIP graph; 'value' above is eager"}
         del g
-    if args.cold:
+    if timing_extras and args.cold:
         # Each step starts after a 1 GiB write that evicts the cache from the
         # 256 MB last-level cache; only the step itself is inside the events.
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -376,22 +364,76 @@ def main():
                        "value": round(kv_bytes / (median(cold_s) * 1e-3) / 1e9, 2), "unit": "GB/s",
                        "note": "each step after a 1 GiB flush write; 'value' and us_per_step above "
                                "are warm (back-to-back steps)"}
-    if w.v_aliases_k:
-        # latent heads run on bf16 MFMA: report the matrix-core share of the
-        # partial pass.  The product P.V runs twice (P as a bf16 hi + lo pair),
-        # so the executed MFMA flops exceed the algorithmic ones.
-        executed = roofline.attention_flops_tokens(w.Hq, seq, T, w.Dqk, 2 * w.Dv)
-        t = partial_avg * 1e-3
-        res["roofline"]["mfma"] = {
-            "busy_frac_counter": MFMA_BUSY.get((w.name, lay_key, kvp, T, khash)),
-            "peak_tflops": roofline.MFMA_BF16_FLOPS / 1e12,
-            "algorithmic_tflops": round(flops / t / 1e12, 2),
-            "algorithmic_frac": round(flops / t / roofline.MFMA_BF16_FLOPS, 4),
-            "executed_tflops": round(executed / t / 1e12, 2),
-            "executed_frac": round(executed / t / roofline.MFMA_BF16_FLOPS, 4),
-            "executed_flops": executed}
-    del dev
+    del dev, o_part, lse_part, o, lse
+    torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    return w, res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first: the clocks settle over the first few dozen launches")
+    ap.add_argument("--workload", default="helix_fp8")
+    ap.add_argument("--kvp", type=int, default=None)
+    ap.add_argument("--layout", default="contiguous", choices=["contiguous", "striped", "staggered16", "paged"],
+                    help="cache layout; a sharded layout views the generated cache as kvp shards of "
+                         "S/kvp rows, the paged layout as a pool of blocks handed to the requests in "
+                         "a seeded random order (same bytes, same per-step traffic)")
+    ap.add_argument("--block-len", type=int, default=16, help="tokens per block of the paged layout")
+    ap.add_argument("--q-tokens", type=int, default=1,
+                    help="query tokens per request (a multi-token turn, causal among the new tokens; "
+                         "the cache's last T tokens are the new ones)")
+    ap.add_argument("--no-append", action="store_true", help="skip timing kvd_append_kv")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="measure only the selected workload (a default run also measures the MXFP4 Helix "
+                         "shape and the latent-head shape, reported under 'workloads')")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step (partial pass + merge) captured once into a HIP graph "
+                         "and replayed; reported under 'graph'")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps that each start with the last-level cache flushed "
+                         "(for workloads whose cache fits in it); reported under 'cold'")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 5 times (the "
+                         "reference kernel for scaling HBM byte counters), and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU's share of the split-KV path; the library runs on one GPU "
+              "and has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration, "launches": 5}))
+        return
+
+    T = args.q_tokens
+    w, head = measure(args, args.workload, args.kvp, T, args.layout, args.block_len)
+    res = {"metric": METRIC, "value": head["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "us_per_step": head["us_per_step"],
+           "hbm_peak_frac": head["hbm_peak_frac"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": head["dtype"], "arith": head["arith"],
+           "data": "synthetic (seeded N(0,1), encoded to the cache format)"}
+    res.update({k: v for k, v in head.items() if k not in res})
+    default_run = (args.workload == "helix_fp8" and args.kvp in (None, 32) and T == 1
+                   and args.layout == "contiguous")
+    if default_run and not args.no_extra:
+        res["workloads"] = {}
+        for name, kvp in EXTRA:
+            _, sub = measure(args, name, kvp, 1, "contiguous", args.block_len, timing_extras=False)
+            res["workloads"][name] = sub
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

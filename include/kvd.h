@@ -176,17 +176,32 @@ typedef struct {
 /* Shard partials: for every request b, shard j < kvp, query token t and
  * query head h, o_part[j,b,t,h,:] = softmax-weighted mean of V over the tokens
  * of shard j that query t sees (fp32) and lse_part[j,b,t,h] = ln sum of
- * exp(x_s) over them (fp32), i.e. the (o_local, lse_local) pair each
- * KV-parallel rank produces. */
+ * exp(x_s) over them (fp32), i.e. the local output and log-sum-exp that each
+ * KV-parallel rank computes over its own slice of the sequence in the Helix
+ * article (section "Sharding the sequence instead").  q, the cache tensors
+ * and seq_lens are read; o_part [kvp,B,T,Hq,Dv] and lse_part [kvp,B,T,Hq]
+ * (device, caller-owned) are written in full, empty shards included (o = 0,
+ * lse = -inf).  Errors: KVD_ERR_INVALID for a malformed problem or a NULL /
+ * misaligned pointer; KVD_ERR_UNSUPPORTED when no kernel handles the shape. */
 int kvd_decode_partial(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
                        const int32_t* seq_lens, float* o_part, float* lse_part,
                        kvd_stream_t stream);
 
-/* Exact log-sum-exp merge of kvp partials for `rows` independent rows:
+/* Exact log-sum-exp merge of kvp partials for `rows` independent rows: the
+ * per-token merge of KV-parallel fragments in the Helix article (section
+ * "Sharding the sequence instead": rescale each fragment's output by the
+ * exponential of its lse relative to the largest, sum, divide by the summed
+ * weights) and the exact merge equation of the pass-KV ring in the "Context
+ * Parallelism for Scalable Million-Token Inference" note (section "Pass-KV
+ * keeps queries local and circulates keys and values"):
  * M = max_j lse_part[j,r]; w_j = exp(lse_part[j,r] - M) (0 for an empty
  * shard); o[r,:] = sum_j w_j o_part[j,r,:] / sum_j w_j; lse[r] = M + ln sum_j
- * w_j; rows whose shards are all empty give o = 0, lse = -inf.  o_part is
- * [kvp,rows,Dv], lse_part [kvp,rows]; Dv % 4 == 0; rows may be 0. */
+ * w_j; rows whose shards are all empty give o = 0, lse = -inf.  Shards are
+ * summed in ascending j, so results are deterministic.  o_part is
+ * [kvp,rows,Dv], lse_part [kvp,rows] (fp32, device); o [rows,Dv], lse [rows]
+ * (fp32, device, written); Dv % 4 == 0; rows may be 0 (nothing is enqueued).
+ * Errors: KVD_ERR_INVALID for kvp outside [1, 4096], rows < 0, a bad Dv, or a
+ * NULL / misaligned pointer when rows > 0. */
 int kvd_lse_merge(int32_t kvp, int64_t rows, int32_t Dv, const float* o_part,
                   const float* lse_part, float* o, float* lse, kvd_stream_t stream);
 
@@ -194,8 +209,17 @@ int kvd_lse_merge(int32_t kvp, int64_t rows, int32_t Dv, const float* o_part,
  * partials, 256-byte aligned pieces); 0 if p is invalid. */
 size_t kvd_decode_workspace_bytes(const kvd_problem* p);
 
-/* kvd_decode_partial into `workspace` followed by kvd_lse_merge (rows =
- * B*T*Hq) into o, lse, both on `stream`: the exact full-context result. */
+/* The whole KV-parallel decode flow of the Helix article (section "Sharding
+ * the sequence instead": every KV-parallel rank runs attention over its shard
+ * and returns its partial output with the log-sum-exp, and the partials are
+ * merged per token into the exact full-context result) on one device:
+ * kvd_decode_partial into `workspace` (o_part at its start, lse_part at the
+ * next 256-byte boundary after kvp*B*T*Hq*Dv floats; the caller allocates
+ * kvd_decode_workspace_bytes(p) device bytes, 16-byte aligned, and owns them)
+ * followed by kvd_lse_merge (rows = B*T*Hq) into o [B,T,Hq,Dv] and lse
+ * [B,T,Hq], both on `stream`.  The workspace holds intermediate values only;
+ * its contents after the call are unspecified.  Validation covers both steps
+ * before anything is enqueued (the same errors as kvd_decode_partial). */
 int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
                const int32_t* seq_lens, void* workspace, float* o, float* lse,
                kvd_stream_t stream);

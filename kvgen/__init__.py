@@ -143,6 +143,47 @@ def encode_e2m1(values) -> np.ndarray:
     return out
 
 
+# ------------------------------------------------ encoding given values
+# Planted test inputs (values chosen by a test rather than drawn from a
+# stream) are encoded by the same rules as the generated tensors.
+def encode_fp8_slab(values):
+    """(codes, scale) of one (request, KV head) slab of given values: scale =
+    amax / 448 in fp32 (1 for an all-zero slab), each code the nearest E4M3 of
+    x / scale (fp32 division), ties to even, saturated to +-448."""
+    x = np.ascontiguousarray(values, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    scale = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    codes = encode_e4m3(x / scale).reshape(x.shape)
+    return codes, scale
+
+
+def pack_mxfp4(codes, exponents):
+    """MXFP4 bytes from E2M1 codes [..., D] (4-bit, sign in bit 3) and E8M0
+    exponents [..., D/32]: (data [..., D/2] with element 2i in the low nibble,
+    scales [..., D/32])."""
+    c = np.asarray(codes, dtype=np.uint8)
+    data = (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
+    return (np.ascontiguousarray(data, dtype=np.uint8),
+            np.ascontiguousarray(np.asarray(exponents), dtype=np.uint8))
+
+
+def encode_mxfp4(values):
+    """MXFP4 rows of given values [..., D] (D % 32 == 0) by the generated rows'
+    rule: per 32-element block E = clamp(floor(log2 amax) - 2 + 127, 0, 254)
+    (127 for an all-zero block) and elements the nearest E2M1 of
+    x 2^(127 - E), ties to even, saturated to +-6."""
+    x = np.asarray(values, dtype=np.float32).astype(np.float64)
+    D = x.shape[-1]
+    assert D % 32 == 0
+    blocks = x.reshape(x.shape[:-1] + (D // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e2 = np.frexp(amax)                       # amax = m 2^e2, m in [0.5, 1)
+    E = np.where(amax > 0, np.clip(e2 - 1 - 2 + 127, 0, 254), 127).astype(np.int64)
+    scaled = blocks * np.ldexp(1.0, (127 - E))[..., None]
+    codes = encode_e2m1(scaled).reshape(x.shape)
+    return pack_mxfp4(codes, E)
+
+
 # -------------------------------------------------------------- workloads
 @dataclass(frozen=True)
 class Workload:

@@ -6,22 +6,31 @@
 // exactly the 16-wide dimension of the gfx950 matrix instructions, so both
 // contractions run on them:
 //
-//   S^T[token, head] = K_tile[token, :] . Q[head, :]
-//   O^T[dv, head]   += V_tile^T[dv, token] . P^T[token, head] (32 tokens, 8 column
-//                                                              blocks x (hi, lo) = 16 MFMAs)
+//   S^T[token, head] = K_tile[token, :] . Q[head, :]     (4 MFMAs / 16 tokens)
+//   O^T[dv, head]   += V_tile^T[dv, token] . P^T[token, head] (32 tokens, 8
+//                                                        column blocks)
 //
-// The logits of a bf16 cache take four v_mfma_f32_16x16x32_bf16 per 16
-// tokens.  An fp8 or MXFP4 K tile is not decoded at all: its bytes are the
-// A operand of the block-scaled v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 with
-// unit scales, or E2M1 with the cache's own E8M0 block exponents), and the
-// bf16 query is the B operand as two E4M3 parts with power-of-two scales
-// whose sum reproduces every query element that matters exactly (split_query),
-// so the logits are exact products summed in fp32 in every format.  V is
-// decoded to bf16 in registers with the hardware converters (exact).  The
-// softmax weights P = exp2(logit - running max) are fp32; the PV product
-// takes them as a bf16 pair hi + lo (two MFMAs), which keeps ~16 significant
-// bits instead of 8, so the output error stays near fp32 level even for short
-// shards.
+// Logits.  The cache's K elements are decoded to bf16 in registers (exact for
+// every format: bf16, E4M3, and E2M1 times its E8M0 block scale) and multiply
+// the bf16 query on v_mfma_f32_16x16x32_bf16, whose products are exact and
+// whose accumulation is fp32-accurate.  (The block-scaled f8f6f4 instruction
+// could take the fp8 / fp4 bytes as they are, but it sums its 128 products
+// with an error of about 2^-13 of the largest one, which large logits turn
+// into visible log-sum-exp errors.)  An fp8 slab's scale is folded into the
+// log2 multiplier of the logits; the query carries its sign.
+//
+// Weights.  P = exp2(logit - running max) in fp32; the running sum of these
+// fp32 weights gives the log-sum-exp.  The PV product takes P
+//  * for fp8 and MXFP4 caches as fp16 (truncated, offset by 2^7 so that
+//    weights down to 2^-31 of the largest are kept), against V decoded to
+//    fp16 (exact for E4M3, and for E2M1 whenever the tile's block exponents
+//    lie in [114, 140]; a tile outside that range takes the bf16 pair below),
+//    one v_mfma_f32_16x16x32_f16 per block, and the output is normalized by
+//    the sum of the same fp16 weights (one more MFMA against a ones operand),
+//    so it is an exact convex combination of the cached values whose weights
+//    are within 2^-10 (relative) of the softmax's;
+//  * for bf16 caches as a bf16 pair hi + lo (two MFMAs), ~16 significant bits,
+//    normalized by the fp32 sum.
 //
 // Work split: one workgroup of 4 waves per (shard j, request b, KV head,
 // chunk of query tokens: one token for a single-token decode, two or four for
@@ -33,7 +42,9 @@
 // Lane (r, g) = (lane % 16, lane / 16):
 //  * K: lane (r, g) loads token r of each 16-token half-tile, bytes
 //    [64i + 16g, 64i + 16g + 16) of the row for each 16-byte load i, so each
-//    load instruction reads 64 contiguous bytes of 16 rows.
+//    load instruction reads 64 contiguous bytes of 16 rows.  MFMA chunk c of
+//    the logits contracts the 8 dims Layout::chunk_d(c, g) of this lane's
+//    bytes (and the query supplies the same dims).
 //  * V: lane (r, g) loads columns [8r, 8r + 8) of the 8 tokens
 //    {4g..4g+3, 16+4g..16+4g+3}, one full row per 16 lanes per instruction, and
 //    regroups them with byte permutes into per-column token octets.
@@ -43,8 +54,8 @@
 //    accumulator of lane (n, g) is head n, dv in [32g, 32g + 32).
 // The running max is only moved when a tile's max exceeds it by more than 2^8
 // (in the exp2 domain); the stale max is exact algebra and keeps P <= 256.
-// At the end the four waves' (max, sum, acc) states are merged through LDS and
-// the normalized partial o and its natural-log lse are written.
+// At the end the four waves' (max, sums, acc) states are merged through LDS
+// and the normalized partial o and its natural-log lse are written.
 #include <type_traits>
 
 #include "kvd_device.hpp"
@@ -54,20 +65,31 @@ namespace kvd {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kD = 128;        // head width (Dqk = Dv)
 constexpr int kTile = 32;      // tokens per wave iteration
 constexpr float kLazyMax = 8.0f;
+// fp16 weights are 2^kPOffset times exp2(logit - running max): at most 2^15
+// (below fp16's largest, 65504) and no smaller than 2^7 for the largest
+// weight, so fp16's smallest subnormal, 2^-24, is 2^-31 of it.
+constexpr float kPOffset = 7.0f;
+// MXFP4 V block exponents whose E2M1 values (0.5 .. 6 times 2^(E-127)) are
+// normal fp16 numbers: E in [kVE16Lo, kVE16Lo + kVE16Span].
+constexpr uint32_t kVE16Lo = 114;
+constexpr uint32_t kVE16Span = 26;
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+__device__ __forceinline__ u32x4_t u4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4_t v = {a, b, c, d};
-  return __builtin_bit_cast(bf16x8_t, v);
+  return v;
+}
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8_t, u4(a, b, c, d));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
@@ -107,32 +129,35 @@ __device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t
 template <int KV>
 struct Layout;
 
-// bf16: 64 B of K per lane per half-tile (4 loads), 16 B of V per token.
+// chunk_d(c, g): first of the 8 consecutive dims that lane group g supplies
+// to MFMA chunk c of the logits (the dims its K loads hold, in order).
+// bf16: 64 B of K per lane per half-tile (4 loads: dims 32i + 8g .. +7 of
+// load i), 16 B of V per token.
 template <>
 struct Layout<kBF16> {
   static constexpr int kRing = 2;       // tiles held in registers (current + prefetched)
   static constexpr int kKLoads = 4;     // 16-byte K loads per lane per half-tile
   static constexpr int kVBytes = 16;    // V bytes per lane per token
   static constexpr int kRowBytes = 256;
-  // first d of MFMA chunk c for lane group g
   __device__ static constexpr int chunk_d(int c, int g) { return 32 * c + 8 * g; }
 };
-// kFmt: the A operand format code of the block-scaled MFMA (cbsz).
+// fp8: lane (r, g) holds dims 16g .. 16g+15 and 64+16g .. 64+16g+15.
 template <>
 struct Layout<kFP8> {
-  static constexpr int kFmt = 0;        // E4M3; lane (r, g) holds dims 16g.. and 64+16g..
-  static constexpr int kRing = 3;
+  static constexpr int kRing = 4;
   static constexpr int kKLoads = 2;
   static constexpr int kVBytes = 8;
   static constexpr int kRowBytes = 128;
+  __device__ static constexpr int chunk_d(int c, int g) { return 64 * (c >> 1) + 16 * g + 8 * (c & 1); }
 };
+// MXFP4: lane (r, g) holds dims 32g .. 32g+31 (one E8M0 block).
 template <>
 struct Layout<kMXFP4> {
-  static constexpr int kFmt = 4;        // E2M1; lane (r, g) holds dims 32g .. 32g+31
-  static constexpr int kRing = 3;
+  static constexpr int kRing = 4;
   static constexpr int kKLoads = 1;
   static constexpr int kVBytes = 4;
   static constexpr int kRowBytes = 64;
+  __device__ static constexpr int chunk_d(int c, int g) { return 32 * g + 8 * c; }
 };
 
 // Raw (undecoded) registers of one 32-token tile for one lane.
@@ -188,134 +213,96 @@ __device__ __forceinline__ int64_t longest_first_unit(int64_t p, const PartialAr
   return ((int64_t)(rem / a.Hkv) * a.B + b) * a.Hkv + rem % a.Hkv;
 }
 
-// LDS of the final merge of the four waves' states.
+// LDS of the final merge of the four waves' states: accumulators, running
+// maxima, fp32 weight sums (for the lse) and the sums the accumulators are
+// normalized by (the fp16 weights' for fp8 / MXFP4 caches).
 struct MergeLds {
   float o[kWaves][16][kD + 4];
   float m[kWaves][16];
   float l[kWaves][16];
+  float ln[kWaves][16];
 };
 
-// bf16 K operand of MFMA chunk c of half-tile u: the 8 dims
-// Layout<kBF16>::chunk_d(c, g) of token 16u + r16.
-__device__ __forceinline__ bf16x8_t k_operand(const Raw<kBF16>& rw, int u, int c) {
-  return as_bf16x8(rw.k[u][4 * c], rw.k[u][4 * c + 1], rw.k[u][4 * c + 2], rw.k[u][4 * c + 3]);
-}
-
-// The K bytes of half-tile u as the A operand of the block-scaled MFMA: an
-// fp8 lane holds 32 E4M3 bytes, an MXFP4 lane 16 bytes (32 E2M1 nibbles, the
-// upper half of the operand unused).
+// K operand of logits chunk c of half-tile u, decoded to bf16: the 8 dims
+// Layout::chunk_d(c, g) of token 16u + r16 (fp8: unscaled codes; MXFP4: times
+// the block's E8M0 scale, E = 0 taken as 0 and E = 255 as +inf).
 template <int KV>
-__device__ __forceinline__ i32x8_t k_bytes(const Raw<KV>& rw, int u) {
-  i32x8_t a;
-#pragma unroll
-  for (int w = 0; w < 8; ++w) a[w] = w < 4 * Layout<KV>::kKLoads ? (int)rw.k[u][w] : 0;
-  return a;
+__device__ __forceinline__ bf16x8_t k_operand(const Raw<KV>& rw, int u, int c) {
+  if constexpr (KV == kBF16) {
+    return as_bf16x8(rw.k[u][4 * c], rw.k[u][4 * c + 1], rw.k[u][4 * c + 2], rw.k[u][4 * c + 3]);
+  } else if constexpr (KV == kFP8) {
+    const uint32_t w0 = rw.k[u][2 * c], w1 = rw.k[u][2 * c + 1];
+    return as_bf16x8(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true)));
+  } else {
+    const uint32_t w = rw.k[u][c];
+    const float sc = e8m0_to_f32_fast(rw.ks[u]);
+    return as_bf16x8(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
+  }
 }
 
-// The query of head n as the B operand of v_mfma_scale_f32_16x16x128_f8f6f4
-// (fp8 and MXFP4 caches).  With 8-bit operands lane group g of that
-// instruction covers the contraction indices {16g .. 16g+15, 64+16g .. 64+16g+15}
-// (bytes 0-15, 16-31) and supplies the E8M0 scale of index block g
-// (32g .. 32g+31); with a 4-bit A operand lane group g covers 32g .. 32g+31.
-// One scale per head, so the per-lane scales agree whatever the grouping.
-// The bf16 query is split as q = hi 2^sh + lo 2^sl, hi and lo OCP E4M3 and
-// round-to-nearest: sh puts the head's largest |q| in [128, 256) hi units and
-// sl = sh - 4.  Where |q| >= 2^(sh-6) (hi normal), the residual q - hi 2^sh is
-// a multiple of q's ulp of at most half an E4M3 ulp of q, so it has at most
-// 4 significant bits and lo holds it exactly: hi 2^sh + lo 2^sl = q.  Smaller
-// elements (below 2^-13 of the head's largest |q|) are off by at most half an
-// E4M3 subnormal step of lo, 2^(sl-10) = 2^(sh-14).
-struct QSplit {
-  i32x8_t hi, lo;
-  int sh, sl;   // E8M0 scale bytes (exponent + 127)
-};
-
-__device__ __forceinline__ QSplit split_query(const uint16_t* qrow, int g) {
-  float x[32];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 64 * h + 16 * g + 8 * k);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[16 * h + 8 * k + 2 * e] = __uint_as_float(w[e] << 16);
-        x[16 * h + 8 * k + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-      }
-    }
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  amax = rows4_max(amax);   // the head's 128 dims sit in its 4 lane groups
-  // floor(log2(amax)) from the exponent field (amax = 0 or fp32-subnormal: the
-  // clamp below takes over)
-  const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127;
-  int sh = e - 7;
-  sh = sh < -123 ? -123 : (sh > 120 ? 120 : sh);
-  const int sl = sh - 4;
-  const float inv_h = __uint_as_float((uint32_t)(127 - sh) << 23);   // 2^-sh, exact
-  QSplit r;
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    float y[4], z[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) y[k] = x[4 * w + k] * inv_h;
-    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    hw = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], hw, true);
-    const f32x2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)hw, 1.0f, false);
-    const f32x2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)hw, 1.0f, true);
-    // residual in lo units (exact: y - hi is on y's grid, 16 a power of two)
-    z[0] = (y[0] - h01[0]) * 16.0f;
-    z[1] = (y[1] - h01[1]) * 16.0f;
-    z[2] = (y[2] - h23[0]) * 16.0f;
-    z[3] = (y[3] - h23[1]) * 16.0f;
-    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
-    lw = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], lw, true);
-    r.hi[w] = hw;
-    r.lo[w] = lw;
-  }
-  r.sh = sh + 127;
-  r.sl = sl + 127;
-  return r;
+// Whether every V block exponent of an MXFP4 tile decodes to normal fp16
+// values (wave-uniform).
+__device__ __forceinline__ bool v_fits_f16(const Raw<kMXFP4>& rw) {
+  const bool ok = (rw.vs[0] - kVE16Lo) <= kVE16Span && (rw.vs[1] - kVE16Lo) <= kVE16Span;
+  return __all(ok);
 }
 
-// V^T operands of the 8 16-column blocks of the PV product, decoded to bf16:
-// f(blk, op) is called for each block as soon as its operand is ready.  The
-// operand of block blk holds the lane's column of that block for the 8 tokens
-// {4g + i, 16 + 4g + i}, in the k order of the P^T operand.
+// V^T operands of the 8 16-column blocks of the PV product, decoded to fp16
+// (F16) or bf16: f(blk, op) is called for each block as soon as its operand
+// (four dwords) is ready.  The operand of block blk holds the lane's column of
+// that block for the 8 tokens {4g + i, 16 + 4g + i}, in the k order of the
+// P^T operand.  fp16 needs fp8 (E4M3 codes are fp16 numbers) or an MXFP4 tile
+// that v_fits_f16; a bf16 cache is bf16 only.
 // MXFP4: lane L of the wave holds the V exponent of (token 16u + L / 4,
 // column block L % 4) in rw.vs[u]; vs_lane is the byte address (for
 // ds_bpermute) of the lane holding this lane's block (r / 4) of token 4g.
-template <int KV, class F>
+template <int KV, bool F16, class F>
 __device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_lane, F&& f) {
-  if constexpr (KV == kBF16 || KV == kMXFP4) {
-    // token-major bf16 pairs cv[e][q] = columns (8 r16 + 2q, 8 r16 + 2q + 1) of token e
-    uint32_t cv[8][4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (KV == kBF16) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cv[e][q] = rw.v[e][q];
-      } else {
-        // token 16 (e / 4) + 4g + e % 4 sits 4 (e % 4) lanes past token 4g
-        const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(vs_lane + 16 * (e % 4)), (int)rw.vs[e / 4]);
-        const float vsc = e8m0_to_f32_fast(x);
-        const uint32_t w = rw.v[e][0];
-        cv[e][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 0));
-        cv[e][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 1));
-        cv[e][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 2));
-        cv[e][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, vsc, 3));
-      }
-    }
+  static_assert(!(F16 && KV == kBF16), "bf16 cache: bf16 V");
+  if constexpr (KV == kBF16) {
+    // rw.v[e][q] = columns (8 r16 + 2q, 8 r16 + 2q + 1) of token e
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       const int q = blk / 2;
       const uint32_t sel = (blk & 1) ? 0x07060302u : 0x05040100u;
-      f(blk, as_bf16x8(perm(cv[1][q], cv[0][q], sel), perm(cv[3][q], cv[2][q], sel),
-                       perm(cv[5][q], cv[4][q], sel), perm(cv[7][q], cv[6][q], sel)));
+      f(blk, u4(perm(rw.v[1][q], rw.v[0][q], sel), perm(rw.v[3][q], rw.v[2][q], sel),
+                perm(rw.v[5][q], rw.v[4][q], sel), perm(rw.v[7][q], rw.v[6][q], sel)));
     }
+  } else if constexpr (KV == kMXFP4) {
+    // the block scale of each of the lane's 8 tokens: token 16 (e / 4) + 4g +
+    // e % 4 sits 4 (e % 4) lanes past token 4g
+    float vsc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vsc[e] = e8m0_to_f32_fast(
+          (uint32_t)__builtin_amdgcn_ds_bpermute((int)(vs_lane + 16 * (e % 4)), (int)rw.vs[e / 4]));
+    // one column pair q (blocks 2q, 2q + 1) at a time: cv[e] = columns
+    // (8 r16 + 2q, 8 r16 + 2q + 1) of token e
+    auto pair = [&](auto q_tag) {
+      constexpr int q = decltype(q_tag)::value;
+      uint32_t cv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (F16)
+          cv[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(rw.v[e][0], vsc[e], q));
+        else
+          cv[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(rw.v[e][0], vsc[e], q));
+      }
+      f(2 * q, u4(perm(cv[1], cv[0], 0x05040100u), perm(cv[3], cv[2], 0x05040100u),
+                  perm(cv[5], cv[4], 0x05040100u), perm(cv[7], cv[6], 0x05040100u)));
+      f(2 * q + 1, u4(perm(cv[1], cv[0], 0x07060302u), perm(cv[3], cv[2], 0x07060302u),
+                      perm(cv[5], cv[4], 0x07060302u), perm(cv[7], cv[6], 0x07060302u)));
+    };
+    pair(std::integral_constant<int, 0>{});
+    pair(std::integral_constant<int, 1>{});
+    pair(std::integral_constant<int, 2>{});
+    pair(std::integral_constant<int, 3>{});
   } else {
     // fp8: interleave bytes of token pairs, then convert both halves
 #pragma unroll
@@ -327,14 +314,46 @@ __device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_la
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const uint32_t x2 = perm(rw.v[2 * rr + 1][q], rw.v[2 * rr][q], sel);
-          lo[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, false));
-          hi[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, true));
+          if constexpr (F16) {
+            lo[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x2, 1.0f, false));
+            hi[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x2, 1.0f, true));
+          } else {
+            lo[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, false));
+            hi[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x2, 1.0f, true));
+          }
         }
-        f(4 * q + s2, as_bf16x8(lo[0], lo[1], lo[2], lo[3]));
-        f(4 * q + s2 + 1, as_bf16x8(hi[0], hi[1], hi[2], hi[3]));
+        f(4 * q + s2, u4(lo[0], lo[1], lo[2], lo[3]));
+        f(4 * q + s2 + 1, u4(hi[0], hi[1], hi[2], hi[3]));
       }
     }
   }
+}
+
+// Weights of one token on one tile in the formats of the PV product.
+struct Weights {
+  u32x4_t h;    // fp16 weights (F16 path) or the bf16 upper halves (pair path)
+  u32x4_t lo;   // pair path: the bf16 remainders
+};
+
+// One 16-column block of O^T += V^T P^T (or, against ones_operand, the sum of
+// the weights): fp16 weights (F16) or the bf16 pair.
+template <bool F16>
+__device__ __forceinline__ f32x4_t pv_mfma(const u32x4_t& v, const Weights& w, f32x4_t acc) {
+  if constexpr (F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, v), __builtin_bit_cast(f16x8_t, w.h),
+                                                  acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v), __builtin_bit_cast(bf16x8_t, w.h),
+                                                  acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v),
+                                                   __builtin_bit_cast(bf16x8_t, w.lo), acc, 0, 0, 0);
+  }
+}
+// The ones operand of the weight-sum product (fp16 or bf16 1.0 in every element).
+template <bool F16>
+__device__ __forceinline__ u32x4_t ones_operand() {
+  const uint32_t one = F16 ? 0x3C003C00u : 0x3F803F80u;
+  return u4(one, one, one, one);
 }
 
 // PAGED: rows are found through the block table (paged cache layout).
@@ -342,18 +361,23 @@ __device__ __forceinline__ void for_v_operands(const Raw<KV>& rw, uint32_t vs_la
 // when one token chunk covers all query tokens.  With several chunks each
 // chunk reads the shard's rows, the loads are plain, and the later chunks of
 // a shard find them in the caches.
-// TW: query tokens per workgroup.  Each wave loads a tile (and decodes its V)
-// once and runs the logits, softmax and PV product of each of the TW tokens on
-// it; every token keeps its own Q operands, softmax state and accumulator.
+// TW: query tokens per workgroup.  Each wave loads a tile (and decodes its K
+// and V) once and runs the logits, softmax and PV product of each of the TW
+// tokens on it; every token keeps its own Q operands, softmax state and
+// accumulators.
 // LDSRING: the tiles ahead wait in an LDS ring filled by direct-to-LDS loads
 // (Ring, bf16 cache) instead of in registers, which leaves the registers to the
 // tokens and keeps several tiles in flight at one wave per SIMD.
 template <int KV, bool PAGED, bool NT, int TW, bool LDSRING>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV != kBF16 && TW == 1 ? 3 : 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV != kBF16 && TW == 1 ? 2 : 1)))
 void gqa_mfma_kernel(PartialArgs a) {
   using Lay = Layout<KV>;
   constexpr int64_t ROW = Lay::kRowBytes;
   constexpr int kRing = TW > 1 ? 2 : Lay::kRing;
+  // fp16 weights against fp16 V (fp8, MXFP4), normalized by their own sum
+  constexpr bool F16PV = KV != kBF16;
+  constexpr int NACC = F16PV ? 9 : 8;      // PV accumulators (+ the weight sum)
+  constexpr float POFF = F16PV ? kPOffset : 0.0f;
 
   MergeLds* mrg;
   uint32_t ring_lds = 0;   // LDSRING: LDS address of this wave's slots
@@ -425,36 +449,33 @@ void gqa_mfma_kernel(PartialArgs a) {
     ksdata = static_cast<const uint8_t*>(a.k_scale) + row0 * (kD / 32);
     vsdata = static_cast<const uint8_t*>(a.v_scale) + row0 * (kD / 32);
   }
-  const float c2 = a.scale_log2 * kscale;  // raw logit -> log2 domain
+  // raw logit -> log2 domain.  A negative fp8 K scale flips the sign of
+  // every logit of the slab: the query operands carry that sign, so the raw
+  // products already are the signed logits and c2 stays >= 0.
+  const float c2 = a.scale_log2 * fabsf(kscale);
+  const uint32_t qsign = kscale < 0.0f ? 0x80008000u : 0u;
 
   // Q^T operands of each token of the chunk (a token past the end of T loads
-  // the last one's): bf16 cache, lane (n, g) holds head n, the 8 d of chunk c
-  // for group g; fp8 and MXFP4 caches, the two E4M3 parts of split_query.
-  constexpr bool SCALED = KV != kBF16;
+  // the last one's): lane (n, g) holds head n, the 8 dims chunk_d(c, g).
   bf16x8_t qop[TW][4];
-  QSplit qs[TW];
 #pragma unroll
   for (int i = 0; i < TW; ++i) {
     const int qt = qt0 + (i < nq ? i : nq - 1);
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.T + qt) * a.Hq + kvh * 16 + r16) * kD;
-    if constexpr (SCALED) {
-      qs[i] = split_query(qrow, g);
-    } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qrow + Lay::chunk_d(c, g));
-        qop[i][c] = as_bf16x8(v.x, v.y, v.z, v.w);
-      }
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + Lay::chunk_d(c, g));
+      qop[i][c] = as_bf16x8(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
     }
   }
 
-  f32x4_t acc[TW][8];
+  f32x4_t acc[TW][NACC];
   float m2[TW];    // running max of this lane's head (log2 domain)
-  float lsum[TW];  // partial sum of P over this lane's tokens
+  float lsum[TW];  // partial sum of the fp32 weights over this lane's tokens
 #pragma unroll
   for (int i = 0; i < TW; ++i) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[i][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NACC; ++k) acc[i][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m2[i] = -INFINITY;
     lsum[i] = 0.0f;
   }
@@ -554,24 +575,18 @@ void gqa_mfma_kernel(PartialArgs a) {
 
   // Logits S^T = K Q^T of query token i of the chunk for the two half-tiles,
   // as 8 values per lane: head n = r16, tokens base + 16u + 4g + i at x[4u + i].
-  // bf16: kop holds the K operands (filled here for one token); fp8 and
-  // MXFP4: two block-scaled MFMAs per half-tile (query parts hi and lo) on the
-  // raw K bytes.
-  auto logits = [&](const Raw<KV>& rw, bf16x8_t (&kop)[2][4], int i, float (&x)[8]) {
+  // kop holds the decoded K operands (TW > 1: decoded once for all tokens);
+  // for one token each operand is decoded next to its MFMA.
+  auto logits = [&](const Raw<KV>& rw, const bf16x8_t (&kop)[2][4], int i, float (&x)[8]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if constexpr (SCALED) {
-        const i32x8_t ka = k_bytes<KV>(rw, u);
-        const int ksc = KV == kMXFP4 ? (int)rw.ks[u] : 127;   // E8M0 1.0 for fp8
-        s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qs[i].hi, s, Lay::kFmt, 0, 0, ksc, 0, qs[i].sh);
-        s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qs[i].lo, s, Lay::kFmt, 0, 0, ksc, 0, qs[i].sl);
-      } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if constexpr (TW == 1) kop[u][c] = k_operand(rw, u, c);
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (TW == 1)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<KV>(rw, u, c), qop[i][c], s, 0, 0, 0);
+        else
           s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u][c], qop[i][c], s, 0, 0, 0);
-        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[4 * u + e] = s[e];
@@ -580,7 +595,9 @@ void gqa_mfma_kernel(PartialArgs a) {
   // Max of the lane's 8 logits of its head, in the log2 domain.  Whether the
   // running max must move is decided on these lane maxima (any lane over its
   // head's max + 2^kLazyMax); only then is the head's tile max reduced over
-  // its 4 lane groups, so all 4 keep the same running max.
+  // its 4 lane groups, so all 4 keep the same running max.  (A lane whose
+  // logits are all masked gives NaN when c2 = 0: no lane is over the max
+  // then, and the reductions skip NaN.)
   auto lane_max2 = [&](const float (&x)[8]) {
     float tmax = x[0];
 #pragma unroll
@@ -588,71 +605,54 @@ void gqa_mfma_kernel(PartialArgs a) {
     return tmax * c2;
   };
   // Move the running max to mn, rescaling the state.
-  auto rescale = [&](float& m, float& l, f32x4_t (&o)[8], float mn) {
+  auto rescale = [&](float& m, float& l, f32x4_t (&o)[NACC], float mn) {
     const float al = fast_exp2(m - mn);
     l *= al;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= al;
+    for (int i = 0; i < NACC; ++i) o[i] *= al;
     m = mn;
   };
-  // Softmax weights P = 2^(x c2 - m) (0 for masked logits) added to the
-  // running sum and split as P = hi + lo: hi keeps the upper 16 bits of each
-  // fp32 weight (exact), lo is the remainder rounded to bf16, so hi + lo
-  // carries ~16 significant bits.
-  auto weights = [&](const float (&x)[8], float m, float& l, bf16x8_t& pop, bf16x8_t& pol, auto mask_tag) {
+  // Softmax weights P = 2^(x c2 - m + POFF) (0 for masked logits), added to
+  // the fp32 running sum and packed for the PV product: F16, as fp16
+  // (truncated); otherwise (bf16 caches, MXFP4 tiles outside the fp16 range)
+  // as the bf16 pair: hi keeps the upper 16 bits of each fp32 weight (exact),
+  // lo the remainder rounded to bf16, so hi + lo carries ~16 significant bits.
+  auto weights = [&](const float (&x)[8], float m, float& l, Weights& w, auto f16_tag, auto mask_tag) {
+    constexpr bool F16 = decltype(f16_tag)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2(fmaf(x[e], c2, -m));
+      p[e] = fast_exp2(fmaf(x[e], c2, POFF - m));
       if constexpr (MASK) p[e] = (x[e] == -INFINITY) ? 0.0f : p[e];
       l += p[e];
     }
     uint32_t ph[4], pl[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const uint32_t b0 = __float_as_uint(p[2 * rr]), b1 = __float_as_uint(p[2 * rr + 1]);
-      ph[rr] = perm(b1, b0, 0x07060302u);
-      pl[rr] = pack_bf16(p[2 * rr] - __uint_as_float(b0 & 0xFFFF0000u),
-                         p[2 * rr + 1] - __uint_as_float(b1 & 0xFFFF0000u));
+      if constexpr (F16) {
+        ph[rr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p[2 * rr], p[2 * rr + 1]));
+      } else {
+        const uint32_t b0 = __float_as_uint(p[2 * rr]), b1 = __float_as_uint(p[2 * rr + 1]);
+        ph[rr] = perm(b1, b0, 0x07060302u);
+        pl[rr] = pack_bf16(p[2 * rr] - __uint_as_float(b0 & 0xFFFF0000u),
+                           p[2 * rr + 1] - __uint_as_float(b1 & 0xFFFF0000u));
+      }
     }
-    pop = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
-    pol = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+    w.h = u4(ph[0], ph[1], ph[2], ph[3]);
+    if constexpr (!F16) w.lo = u4(pl[0], pl[1], pl[2], pl[3]);
+  };
+  // Whether this tile's PV product runs on fp16 (wave-uniform).
+  auto tile_f16 = [&](const Raw<KV>& rw) -> bool {
+    if constexpr (KV == kFP8) return true;
+    else if constexpr (KV == kMXFP4) return v_fits_f16(rw);
+    else return false;
   };
 
-  // One query token on one tile: logits, the online softmax update of head
-  // n = r16 over tokens base + 16u + 4g + i, and O^T += V^T P^T, each K and V
-  // operand decoded next to its use.  MASK: rows from nvalid on are not seen
-  // (zero weight).  The running max only moves when a tile's max exceeds it
-  // by more than 2^kLazyMax (in the exp2 domain).
-  auto token_tile = [&](const Raw<KV>& rw, bf16x8_t (&kop)[2][4], float& m, float& l, f32x4_t (&o)[8], int nvalid,
-                        auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    float x[8];
-    logits(rw, kop, 0, x);
-    if constexpr (MASK) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * u + 4 * g + i >= nvalid) x[4 * u + i] = -INFINITY;
-    }
-    const float lmax2 = lane_max2(x);
-    if (__any(lmax2 > m + kLazyMax)) rescale(m, l, o, fmaxf(m, rows4_max(lmax2)));
-    bf16x8_t pop, pol;
-    weights(x, m, l, pop, pol, mask_tag);
-    // one MFMA pair per 16-column block
-    auto pv = [&](int blk, const bf16x8_t& v) {
-      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop, o[blk], 0, 0, 0);
-      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pol, o[blk], 0, 0, 0);
-    };
-    for_v_operands<KV>(rw, vs_lane, pv);
-  };
-
-  // Every token of the chunk on one tile, phase by phase: the K operands (bf16:
-  // repacked once; fp8, MXFP4: the raw bytes) for the logits of all tokens, one
-  // rescale check, the weights of all, then V
-  // decoded block by block straight into every token's PV product.  The
+  // Every token of the chunk on one tile, phase by phase: the K operands
+  // (decoded once for all tokens when TW > 1) for the logits of all tokens,
+  // one rescale check, the weights of all, then V decoded block by block
+  // straight into every token's PV product (and the weight sums).  The
   // tokens' independent MFMA chains interleave, and neither all K nor all V
   // operands are held at once.  MASK: token i sees the tile's rows below
   // nv[i] only (none when nv[i] <= 0).
@@ -661,11 +661,11 @@ void gqa_mfma_kernel(PartialArgs a) {
     float x[TW][8];
     {
       bf16x8_t kop[2][4];
-      if constexpr (!SCALED) {
+      if constexpr (TW > 1) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) kop[u][c] = k_operand(rw, u, c);
+          for (int c = 0; c < 4; ++c) kop[u][c] = k_operand<KV>(rw, u, c);
       }
 #pragma unroll
       for (int i = 0; i < TW; ++i) logits(rw, kop, i, x[i]);
@@ -693,20 +693,36 @@ void gqa_mfma_kernel(PartialArgs a) {
         if (__any(tmax2 > m2[i] + kLazyMax)) rescale(m2[i], lsum[i], acc[i], fmaxf(m2[i], tmax2));
       }
     }
-    bf16x8_t pop[TW], pol[TW];
+    if constexpr (F16PV) {
+      if (tile_f16(rw)) {
+        Weights wf[TW];
 #pragma unroll
-    for (int i = 0; i < TW; ++i) weights(x[i], m2[i], lsum[i], pop[i], pol[i], mask_tag);
-    for_v_operands<KV>(rw, vs_lane, [&](int blk, const bf16x8_t& v) {
+        for (int i = 0; i < TW; ++i) weights(x[i], m2[i], lsum[i], wf[i], std::true_type{}, mask_tag);
+        for_v_operands<KV, true>(rw, vs_lane, [&](int blk, const u32x4_t& v) {
 #pragma unroll
-      for (int i = 0; i < TW; ++i) {
-        acc[i][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop[i], acc[i][blk], 0, 0, 0);
-        acc[i][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pol[i], acc[i][blk], 0, 0, 0);
+          for (int i = 0; i < TW; ++i) acc[i][blk] = pv_mfma<true>(v, wf[i], acc[i][blk]);
+        });
+#pragma unroll
+        for (int i = 0; i < TW; ++i) acc[i][8] = pv_mfma<true>(ones_operand<true>(), wf[i], acc[i][8]);
+        return;
       }
+    }
+    // bf16 V against the bf16 pair
+    Weights wb[TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) weights(x[i], m2[i], lsum[i], wb[i], std::false_type{}, mask_tag);
+    for_v_operands<KV, false>(rw, vs_lane, [&](int blk, const u32x4_t& v) {
+#pragma unroll
+      for (int i = 0; i < TW; ++i) acc[i][blk] = pv_mfma<false>(v, wb[i], acc[i][blk]);
     });
+    if constexpr (F16PV) {
+#pragma unroll
+      for (int i = 0; i < TW; ++i) acc[i][8] = pv_mfma<false>(ones_operand<false>(), wb[i], acc[i][8]);
+    }
   };
 
-  // MASK: the tile runs past the shard end (single token: its extra tokens get
-  // zero weight).  With several tokens every token checks its own cut.
+  // MASK: the tile runs past the shard end, or past a token's cut: rows at or
+  // past a token's cut get weight 0.
   using Masked = std::true_type;      // compute: rows past a token's cut get weight 0
   using Unmasked = std::false_type;
   using FullTile = std::true_type;    // load: every row of the tile inside the shard
@@ -715,16 +731,17 @@ void gqa_mfma_kernel(PartialArgs a) {
   using Unclamped = std::false_type;
   auto compute = [&](const Raw<KV>& rw, int tile, auto mask_tag) {
     const int64_t base = s0 + (int64_t)tile * kTile;
-    if constexpr (TW == 1) {
-      bf16x8_t kop[2][4];
-      token_tile(rw, kop, m2[0], lsum[0], acc[0], (int)(s1 - base), mask_tag);
-    } else {
-      int nv[TW];
+    int nv[TW];
 #pragma unroll
-      for (int i = 0; i < TW; ++i) {
-        const int64_t n = s1t[i] - base;         // wave-uniform
-        nv[i] = n < 0 ? 0 : (n > kTile ? kTile : (int)n);
-      }
+    for (int i = 0; i < TW; ++i) {
+      const int64_t n = s1t[i] - base;         // wave-uniform
+      nv[i] = n < 0 ? 0 : (n > kTile ? kTile : (int)n);
+    }
+    if constexpr (TW == 1 && decltype(mask_tag)::value) {
+      tokens_tile(rw, nv, Masked{});
+    } else if constexpr (TW == 1) {
+      tokens_tile(rw, nv, Unmasked{});
+    } else {
       if (nv[0] == kTile)                        // every token sees the whole tile
         tokens_tile(rw, nv, Unmasked{});
       else
@@ -836,35 +853,21 @@ void gqa_mfma_kernel(PartialArgs a) {
     if (nfull > 0) {
       auto clampt = [&](int t) { return t < nfull - 1 ? t : nfull - 1; };
       int tile = wave;
-      if constexpr (kRing == 2) {
-        Raw<KV> ra, rb;
-        load(ra, clampt(tile), FullTile{});
-        while (tile < nfull) {
-          load(rb, clampt(tile + kWaves), FullTile{});
-          compute(ra, tile, Unmasked{});
-          tile += kWaves;
-          if (tile >= nfull) break;
-          load(ra, clampt(tile + kWaves), FullTile{});
-          compute(rb, tile, Unmasked{});
-          tile += kWaves;
-        }
-      } else {
-        static_assert(kRing == 3, "ring of 2 or 3 buffers");
-        Raw<KV> ra, rb, rc;
-        load(ra, clampt(tile), FullTile{});
-        load(rb, clampt(tile + kWaves), FullTile{});
-        while (tile < nfull) {
-          load(rc, clampt(tile + 2 * kWaves), FullTile{});
-          compute(ra, tile, Unmasked{});
-          tile += kWaves;
-          if (tile >= nfull) break;
-          load(ra, clampt(tile + 2 * kWaves), FullTile{});
-          compute(rb, tile, Unmasked{});
-          tile += kWaves;
-          if (tile >= nfull) break;
-          load(rb, clampt(tile + 2 * kWaves), FullTile{});
-          compute(rc, tile, Unmasked{});
-          tile += kWaves;
+      // rb[k] holds tile wave + (n kRing + k) kWaves; the loop body is
+      // unrolled kRing times so that every buffer index is a constant
+      Raw<KV> rb[kRing];
+#pragma unroll
+      for (int k = 0; k < kRing - 1; ++k) load(rb[k], clampt(tile + k * kWaves), FullTile{});
+      bool more = tile < nfull;
+      while (more) {
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) {
+          if (more) {
+            load(rb[(k + kRing - 1) % kRing], clampt(tile + (kRing - 1) * kWaves), FullTile{});
+            compute(rb[k], tile, Unmasked{});
+            tile += kWaves;
+            more = tile < nfull;
+          }
         }
       }
     }
@@ -888,6 +891,9 @@ void gqa_mfma_kernel(PartialArgs a) {
     if (g == 0) {
       mrg->m[wave][r16] = m2[i];
       mrg->l[wave][r16] = lw;
+      // F16PV: the sum of the fp16 weights, the same in every element of the
+      // weight-sum accumulator of head r16
+      mrg->ln[wave][r16] = F16PV ? acc[i][NACC - 1][0] : lw;
     }
     __syncthreads();
     const int64_t orow0 = (((int64_t)j * a.B + b) * a.T + qt0 + i) * a.Hq + kvh * 16;   // o_part / lse_part row
@@ -904,7 +910,7 @@ void gqa_mfma_kernel(PartialArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           const float f = rescale_weight(mrg->m[w][n], M);
-          lt += mrg->l[w][n] * f;
+          lt += mrg->ln[w][n] * f;
           ot += mrg->o[w][n][d] * f;
         }
         o = ot / lt * vscale;
@@ -920,7 +926,7 @@ void gqa_mfma_kernel(PartialArgs a) {
         float lt = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) lt += mrg->l[w][tid] * rescale_weight(mrg->m[w][tid], M);
-        lse = (M + fast_log2(lt)) * kLn2;
+        lse = (M - POFF + fast_log2(lt)) * kLn2;
       }
       a.lse_part[orow0 + tid] = lse;
     }

@@ -258,21 +258,80 @@ def _check_sampled(name, kvp, n_pairs=3):
                    "%s kvp=%d b=%d kvh=%d partials" % (name, kvp, b, kvh))
 
 
+# Planted peak logits (nats) per query head of the peaked check, in turn; 0
+# keeps the generated query.  With N(0,1) keys at these widths the other
+# logits are N(0, (peak / |k[s*]|)^2), so over 2^19..2^20 tokens the planted
+# token carries from about half (15) to all but ~e^-13 (30) of the weight.
+PEAKS = (0.0, 15.0, 20.0, 30.0)
+
+
+def _check_peaked(name, kvp, n_pairs=2):
+    """The full-size cache with the softmax concentrated on one cached token
+    per query head: for the heads of the sampled (request, KV head) slabs the
+    query becomes beta k[s*] for a seeded position s*, with beta chosen so that
+    the planted logit sm_scale q.k[s*] is 15, 20 or 30 nats (one head in four
+    keeps its N(0,1) query).  Outputs are then O(1) (a few cached values
+    dominate), so the absolute output bound is a tight check; the shards
+    without s* still see N(0,1) logits."""
+    import dataclasses
+    import torch
+    import oracle
+    dev = _device_inputs(name)
+    w = dev.workload
+    assert w.q_dtype == "bf16" and w.q_tokens == 1
+    seq = dev.seq_lens.cpu().numpy()
+    q_np = dev.q.cpu().numpy().view(np.uint16).copy()
+    sm = oracle.default_scale(w.Dqk)
+    rng = np.random.default_rng(2024 + kvp)
+    pairs = gc.sampled_pairs(w, n_pairs, seed=kvp)
+    G = w.G
+    for (b, kvh) in pairs:
+        kd, ks = kvgen.gen_kv_slab(w, "k", b, kvh)
+        L = int(seq[b])
+        for i in range(G):
+            peak = PEAKS[i % len(PEAKS)]
+            if peak == 0.0:
+                continue
+            s = int(rng.integers(L))
+            sc = ks if w.kv_dtype in ("fp8", "bf16", "f32") else ks[s:s + 1]
+            krow = oracle.dequant(w.kv_dtype, kd[s:s + 1], sc, w.Dqk)[0]
+            beta = peak / (sm * float(krow @ krow))
+            q_np[b, kvh * G + i] = torch.from_numpy((krow * beta).astype(np.float32)).to(
+                torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    dev_p = dataclasses.replace(dev, q=torch.from_numpy(q_np.view(np.int16)).cuda())
+    gc.log("%s kvp=%d peaked: running the library" % (name, kvp))
+    o_part, lse_part, o, lse = gc.run_library(dev_p, kvp)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for (b, kvh) in pairs:
+        gc.log("  oracle on request %d, KV head %d (L=%d), peaked queries" % (b, kvh, seq[b]))
+        ro, rl, parts = gc.oracle_slab(w, b, kvh, seq[b], q_np, kvp)
+        hs = slice(kvh * G, (kvh + 1) * G)
+        assert np.abs(ro).max() > 0.5, "planted peaks should give O(1) outputs"
+        gc.compare(o[b, hs], lse[b, hs], ro, rl, w.kv_dtype, "%s kvp=%d b=%d kvh=%d peaked" % (name, kvp, b, kvh))
+        po = np.stack([p_[0] for p_ in parts])
+        pl = np.stack([p_[1] for p_ in parts])
+        gc.compare(o_part[:, b, hs], lse_part[:, b, hs], po, pl, w.kv_dtype,
+                   "%s kvp=%d b=%d kvh=%d peaked partials" % (name, kvp, b, kvh))
+
+
 @pytest.mark.slow
 def test_full_gqa_bf16_varlen():
     _check_sampled("gqa_bf16_varlen", 16)
+    _check_peaked("gqa_bf16_varlen", 16)
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("kvp", [8, 32, 128])
 def test_full_helix_fp8(kvp):
     _check_sampled("helix_fp8", kvp, n_pairs=2)
+    _check_peaked("helix_fp8", kvp)
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("kvp", [8, 32, 128])
 def test_full_helix_mxfp4(kvp):
     _check_sampled("helix_mxfp4", kvp, n_pairs=2)
+    _check_peaked("helix_mxfp4", kvp)
 
 
 @pytest.mark.slow
@@ -297,3 +356,4 @@ def test_full_mla_bf16():
     if kvd.lib().kvd_decode_workspace_bytes(ctypes.byref(p)) == 0:
         pytest.fail("invalid MLA problem")
     _check_sampled("mla_bf16", 32, n_pairs=2)
+    _check_peaked("mla_bf16", 32, n_pairs=1)

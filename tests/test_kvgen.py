@@ -114,3 +114,27 @@ def test_poison_tail():
     inp = kvgen.poison_tail(kvgen.make_inputs(w))
     assert (inp.k_data[1, :, 17:] == 0x7F).all() and (inp.k_data[1, :, :17] != 0x7F).all()
     assert (inp.v_data[0] != 0x7F).all()
+
+
+def test_encoders_of_given_values_match_generated_encodings():
+    """encode_fp8_slab / encode_mxfp4 of the stream's fp32 values reproduce the
+    generator's own fp8 slab and MXFP4 rows byte for byte (planted inputs are
+    encoded by the same rules as generated ones)."""
+    seed, stream, S, D = 77, 1, 96, 128
+    vals = kvgen.normals_f32(seed, stream, 0, S * D).reshape(S, D)
+    codes, scale = kvgen.fp8_slabs(seed, stream, 0, 1, S * D)
+    c2, s2 = kvgen.encode_fp8_slab(vals)
+    assert np.float32(s2) == scale[0]
+    assert np.array_equal(c2.ravel(), codes)
+    data, sc = kvgen.mxfp4_rows(seed, stream, 0, S, D)
+    d2, sc2 = kvgen.encode_mxfp4(vals)
+    assert np.array_equal(d2.ravel(), data) and np.array_equal(sc2.ravel(), sc)
+
+
+def test_pack_mxfp4_nibble_order_and_zero_block():
+    codes = np.arange(64, dtype=np.uint8).reshape(2, 32) % 16
+    data, sc = kvgen.pack_mxfp4(codes, [[254], [0]])
+    assert data.shape == (2, 16) and sc.tolist() == [[254], [0]]
+    assert data[0, 0] == (0 | (1 << 4)) and data[1, 7] == (14 | (15 << 4))
+    d0, s0 = kvgen.encode_mxfp4(np.zeros((1, 64), np.float32))
+    assert (d0 == 0).all() and (s0 == 127).all()
