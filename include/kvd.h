@@ -115,7 +115,11 @@
 extern "C" {
 #endif
 
-#define KVD_ABI_VERSION 4
+#define KVD_ABI_VERSION 5
+
+/* Bytes of the static device array behind kvd_decode_noalloc (96 MiB per
+ * device the library runs on). */
+#define KVD_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
 
 typedef enum {
   KVD_OK = 0,
@@ -223,6 +227,22 @@ size_t kvd_decode_workspace_bytes(const kvd_problem* p);
 int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
                const int32_t* seq_lens, void* workspace, float* o, float* lse,
                kvd_stream_t stream);
+
+/* kvd_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * shard partials go to a static device array of KVD_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each device it runs on, from the first call on
+ * that device until the process ends; nothing is allocated or freed by the
+ * call.  Arguments, layouts, results and errors are those of kvd_decode
+ * without the workspace, plus KVD_ERR_UNSUPPORTED (nothing enqueued) when
+ * kvd_decode_workspace_bytes(p) exceeds KVD_NOALLOC_SCRATCH_BYTES.  All calls
+ * on one device share that array, and every call overwrites all of the part
+ * it uses before reading it (no state carries over between calls); calls
+ * whose work can overlap on one device (different streams, or different host
+ * threads without ordering) race on it and must be serialized by the caller,
+ * e.g. by issuing them on one stream. */
+int kvd_decode_noalloc(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v,
+                       const int32_t* seq_lens, float* o, float* lse, kvd_stream_t stream);
 
 /* Append T = q_tokens new tokens per request to the cache (the decode step's
  * KV write, or the new tokens of a multi-token turn).  For every request b,

@@ -1,6 +1,9 @@
 // C ABI of libkvd.so (declared in include/kvd.h): host-side validation,
 // kernel selection and launches.  No device memory is read or written here and
-// nothing is allocated; every launch goes onto the caller's stream.
+// nothing is allocated at run time; every launch goes onto the caller's
+// stream.  The one piece of device memory the library owns is the static
+// partials array of kvd_decode_noalloc (below), which the code-object loader
+// places on each device the library runs on.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -9,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kvd.h"
 #include "kvd_internal.hpp"
@@ -241,6 +245,49 @@ size_t workspace_lse_bytes(const kvd_problem* p) {
 
 }  // namespace
 
+// Shard partials of kvd_decode_noalloc: one copy per device (the loader
+// allocates it with the code object; it lives until the process ends).  In
+// host code this name is only a handle for hipGetSymbolAddress: kernels and
+// copies take the device address that call returns (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[KVD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr with an error message
+// if the lookup fails.
+void* noalloc_scratch(int* status) {
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = fail(KVD_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = fail(KVD_ERR_UNSUPPORTED, "device %d is beyond the %d devices kvd_decode_noalloc serves", dev,
+                   kMaxDevices);
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (err[dev] != hipSuccess || addr[dev] == nullptr) {
+    *status = fail(KVD_ERR_HIP, "hipGetSymbolAddress of the static partials failed on device %d: %s", dev,
+                   hipGetErrorString(err[dev]));
+    return nullptr;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 int kvd_abi_version(void) { return KVD_ABI_VERSION; }
@@ -351,6 +398,24 @@ int kvd_decode(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v, const in
   s = launch_partial(p, q, k, v, seq_lens, o_part, lse_part, reinterpret_cast<hipStream_t>(stream));
   if (s != KVD_OK) return s;
   return kvd_lse_merge(p->kvp, rows, p->Dv, o_part, lse_part, o, lse, stream);
+}
+
+int kvd_decode_noalloc(const kvd_problem* p, const void* q, kvd_kv k, kvd_kv v, const int32_t* seq_lens,
+                       float* o, float* lse, kvd_stream_t stream) {
+  int s = check_problem(p);
+  if (s != KVD_OK) return s;
+  s = check_tensors(p, q, k, v, seq_lens);
+  if (s != KVD_OK) return s;
+  const size_t need = workspace_o_bytes(p) + workspace_lse_bytes(p);
+  if (need > (size_t)KVD_NOALLOC_SCRATCH_BYTES)
+    return fail(KVD_ERR_UNSUPPORTED,
+                "kvd_decode_noalloc: the shard partials need %zu bytes, more than its %zu-byte static array "
+                "(kvp*B*q_tokens*Hq*(Dv+1) floats); use kvd_decode with a workspace",
+                need, (size_t)KVD_NOALLOC_SCRATCH_BYTES);
+  void* ws = noalloc_scratch(&s);
+  if (ws == nullptr) return s;
+  // from here on exactly kvd_decode with the static array as its workspace
+  return kvd_decode(p, q, k, v, seq_lens, ws, o, lse, stream);
 }
 
 }  // extern "C"

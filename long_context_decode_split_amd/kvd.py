@@ -30,8 +30,11 @@ LAYOUT_CODES = {"contiguous": KVD_LAYOUT_CONTIGUOUS, "striped": KVD_LAYOUT_STRIP
 
 # Every symbol include/kvd.h declares.
 EXPORTED = ("kvd_decode_partial", "kvd_lse_merge", "kvd_decode_workspace_bytes", "kvd_decode",
+            "kvd_decode_noalloc",
             "kvd_append_kv", "kvd_status_string", "kvd_last_error", "kvd_abi_version")
-ABI_VERSION = 4
+ABI_VERSION = 5
+# KVD_NOALLOC_SCRATCH_BYTES of kvd.h: the static partials of kvd_decode_noalloc
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024
 
 
 class KvdProblem(ctypes.Structure):
@@ -79,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.kvd_decode_workspace_bytes.restype = ctypes.c_size_t
         L.kvd_decode.argtypes = [P, vp, KvdKV, KvdKV, vp, vp, vp, vp, vp]
         L.kvd_decode.restype = ctypes.c_int
+        L.kvd_decode_noalloc.argtypes = [P, vp, KvdKV, KvdKV, vp, vp, vp, vp]
+        L.kvd_decode_noalloc.restype = ctypes.c_int
         L.kvd_append_kv.argtypes = [P, vp, vp, vp, KvdKV, KvdKV, vp]
         L.kvd_append_kv.restype = ctypes.c_int
         L.kvd_status_string.argtypes = [ctypes.c_int]
@@ -162,6 +167,11 @@ def kvd_decode_workspace_bytes(p: KvdProblem) -> int:
 def kvd_decode(p: KvdProblem, q, k, v, seq_lens, workspace, o, lse, stream=None) -> None:
     _check(lib().kvd_decode(ctypes.byref(p), _ptr(q), _kv(k), _kv(v), _ptr(seq_lens), _ptr(workspace),
                             _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def kvd_decode_noalloc(p: KvdProblem, q, k, v, seq_lens, o, lse, stream=None) -> None:
+    _check(lib().kvd_decode_noalloc(ctypes.byref(p), _ptr(q), _kv(k), _kv(v), _ptr(seq_lens), _ptr(o),
+                                    _ptr(lse), _stream(stream)))
 
 
 def kvd_append_kv(p: KvdProblem, k_new, v_new, positions, k, v, stream=None) -> None:

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvd.kvd_abi_version() == kvd.ABI_VERSION == 4
+    assert kvd.kvd_abi_version() == kvd.ABI_VERSION == 5
     for s in range(4):
         assert kvd.kvd_status_string(s).startswith(("KVD_OK", "KVD_ERR"))
     assert "unknown" in kvd.kvd_status_string(99)
