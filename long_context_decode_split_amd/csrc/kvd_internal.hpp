@@ -29,6 +29,9 @@ struct PartialArgs {
   int32_t log2_block;           // block_len = 1 << log2_block
   int32_t max_blocks;
   int64_t num_blocks;
+  // set by the launcher of the matrix-core GQA kernel: consecutive shards
+  // one wave streams when it takes whole shards (0 otherwise)
+  int32_t solo_shards;
 };
 
 // Arguments of one append (kvd_append_kv), already validated by api.cpp.

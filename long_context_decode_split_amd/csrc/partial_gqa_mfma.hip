@@ -133,8 +133,24 @@ struct Layout;
 // to MFMA chunk c of the logits (the dims its K loads hold, in order).
 // bf16: 64 B of K per lane per half-tile (4 loads: dims 32i + 8g .. +7 of
 // load i), 16 B of V per token.
+// Occupancy of the one-token instances: kWavesPerEu, the waves per SIMD the
+// registers are sized for; kLdsReserve, dynamic LDS reserved per workgroup
+// (0: none; above half the CU's LDS it keeps one workgroup, i.e. one wave,
+// per SIMD); kSoloWaves, the wave count from which one-wave shard groups
+// replace the four-wave split (0: never); kStash, the finished shard
+// partials a one-wave group keeps in LDS before writing them out (each batch
+// of stores a wave issues costs it about as long as its writes take to drain,
+// tens of microseconds under a full read stream, because later loads are
+// counted behind the stores).  Measured: the fp8 pass streams
+// best at one wave per SIMD (two waves per SIMD do not share the issue
+// fairly: one of them runs far ahead and the other finishes alone), the
+// MXFP4 pass, with twice the arithmetic per byte, at two.
 template <>
 struct Layout<kBF16> {
+  static constexpr int kWavesPerEu = 1;
+  static constexpr int kLdsReserve = 0;
+  static constexpr int kSoloWaves = 0;
+  static constexpr int kStash = 1;
   static constexpr int kRing = 2;       // tiles held in registers (current + prefetched)
   static constexpr int kKLoads = 4;     // 16-byte K loads per lane per half-tile
   static constexpr int kVBytes = 16;    // V bytes per lane per token
@@ -144,6 +160,10 @@ struct Layout<kBF16> {
 // fp8: lane (r, g) holds dims 16g .. 16g+15 and 64+16g .. 64+16g+15.
 template <>
 struct Layout<kFP8> {
+  static constexpr int kWavesPerEu = 1;
+  static constexpr int kLdsReserve = 96 * 1024;
+  static constexpr int kSoloWaves = 1024;
+  static constexpr int kStash = 4;
   static constexpr int kRing = 4;
   static constexpr int kKLoads = 2;
   static constexpr int kVBytes = 8;
@@ -153,6 +173,10 @@ struct Layout<kFP8> {
 // MXFP4: lane (r, g) holds dims 32g .. 32g+31 (one E8M0 block).
 template <>
 struct Layout<kMXFP4> {
+  static constexpr int kWavesPerEu = 2;
+  static constexpr int kLdsReserve = 0;
+  static constexpr int kSoloWaves = 2048;
+  static constexpr int kStash = 2;
   static constexpr int kRing = 4;
   static constexpr int kKLoads = 1;
   static constexpr int kVBytes = 4;
@@ -195,9 +219,9 @@ typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 // all have one length, keep the plain (shard-major) order.  Every unit keeps
 // its (shard, KV head) and every request keeps its units, so this only
 // permutes which workgroup does which unit.
-__device__ __forceinline__ int64_t longest_first_unit(int64_t p, const PartialArgs& a) {
+// per: units of one request (shard or shard-group positions times Hkv).
+__device__ __forceinline__ int64_t longest_first_unit(int64_t p, const PartialArgs& a, int per) {
   if (a.B <= 1 || a.B > 64) return p;
-  const int per = a.kvp * a.Hkv;
   const int r = (int)(p / per);
   const int rem = (int)(p - (int64_t)r * per);
   const int lane = threadIdx.x & 63;
@@ -212,6 +236,13 @@ __device__ __forceinline__ int64_t longest_first_unit(int64_t p, const PartialAr
   const int b = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
   return ((int64_t)(rem / a.Hkv) * a.B + b) * a.Hkv + rem % a.Hkv;
 }
+
+// One stashed shard partial in LDS: 16 rows (heads) of kD floats, padded to
+// kStashRow, then the 16 lse values.
+constexpr int kStashRow = kD + 4;
+constexpr int kStashFloats = 16 * kStashRow + 16;
+template <int KV>
+constexpr size_t stash_bytes() { return (size_t)kWaves * Layout<KV>::kStash * kStashFloats * sizeof(float); }
 
 // LDS of the final merge of the four waves' states: accumulators, running
 // maxima, fp32 weight sums (for the lse) and the sums the accumulators are
@@ -368,8 +399,14 @@ __device__ __forceinline__ u32x4_t ones_operand() {
 // LDSRING: the tiles ahead wait in an LDS ring filled by direct-to-LDS loads
 // (Ring, bf16 cache) instead of in registers, which leaves the registers to the
 // tokens and keeps several tiles in flight at one wave per SIMD.
-template <int KV, bool PAGED, bool NT, int TW, bool LDSRING>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV != kBF16 && TW == 1 ? 2 : 1)))
+// SOLO (one query token): each wave takes a whole shard unit (unit
+// 4 blockIdx + wave) and streams its tiles in order, then writes the partial
+// from its registers: no LDS and no barrier.  Used when there are enough
+// units to keep every SIMD streaming (short shards, large kvp), where the
+// four-wave merge and the per-workgroup set-up of the default split cost more
+// than they save.
+template <int KV, bool PAGED, bool NT, int TW, bool LDSRING, bool SOLO>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TW == 1 ? Layout<KV>::kWavesPerEu : 1)))
 void gqa_mfma_kernel(PartialArgs a) {
   using Lay = Layout<KV>;
   constexpr int64_t ROW = Lay::kRowBytes;
@@ -379,14 +416,17 @@ void gqa_mfma_kernel(PartialArgs a) {
   constexpr int NACC = F16PV ? 9 : 8;      // PV accumulators (+ the weight sum)
   constexpr float POFF = F16PV ? kPOffset : 0.0f;
 
-  MergeLds* mrg;
+  static_assert(!SOLO || (TW == 1 && !LDSRING), "one-wave units: one query token, register ring");
+  // tile i of a wave's sequence is tile first + i * kStride of its shard
+  constexpr int kStride = SOLO ? 1 : kWaves;
+  MergeLds* mrg = nullptr;
   uint32_t ring_lds = 0;   // LDSRING: LDS address of this wave's slots
   if constexpr (LDSRING) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
     mrg = reinterpret_cast<MergeLds*>(dyn_lds);   // reused once the ring is drained
     ring_lds = (uint32_t)(uintptr_t)(lds_u8*)dyn_lds +
                (uint32_t)(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * Ring::kWaveBytes);
-  } else {
+  } else if constexpr (!SOLO) {
     __shared__ MergeLds st;
     mrg = &st;
   }
@@ -401,11 +441,22 @@ void gqa_mfma_kernel(PartialArgs a) {
   const int nchunks = (a.T + TW - 1) / TW;
   int64_t unit;
   int chunk;
-  if (!unit_token(blockIdx.x, (int64_t)a.kvp * a.B * a.Hkv, nchunks, &unit, &chunk)) return;
-  unit = longest_first_unit(unit, a);
+  // SOLO: a unit is a group of solo_shards consecutive shards of one (request,
+  // KV head); njp groups per (request, KV head)
+  const int njp = SOLO ? (a.kvp + a.solo_shards - 1) / a.solo_shards : a.kvp;
+  if constexpr (SOLO) {
+    unit = (int64_t)blockIdx.x * kWaves + wave;
+    chunk = 0;
+    if (unit >= (int64_t)njp * a.B * a.Hkv) return;   // the whole wave: no barrier follows
+  } else {
+    if (!unit_token(blockIdx.x, (int64_t)a.kvp * a.B * a.Hkv, nchunks, &unit, &chunk)) return;
+  }
+  unit = longest_first_unit(unit, a, njp * a.Hkv);
+  const int first = SOLO ? 0 : wave;                // first tile of this wave
   const int kvh = (int)(unit % a.Hkv);
   const int b = (int)(unit / a.Hkv % a.B);
-  const int j = (int)(unit / ((int64_t)a.Hkv * a.B));
+  // shard (SOLO: first shard of the group)
+  const int j = (int)(unit / ((int64_t)a.Hkv * a.B)) * (SOLO ? a.solo_shards : 1);
   const int qt0 = chunk * TW;                       // first query token of the chunk
   const int nq = a.T - qt0 < TW ? a.T - qt0 : TW;   // tokens of the chunk that exist
 
@@ -414,25 +465,35 @@ void gqa_mfma_kernel(PartialArgs a) {
   // bounds the rows read; tokens past the end of T see none.
   const int64_t L = a.seq_lens[b];
   const ShardSpan span = shard_span(a.layout, L, a.T, qt0 + nq - 1, a.S_max, a.kvp, a.B, a.Hkv, j, b, kvh);
-  const int64_t s0 = span.s0, s1 = span.s1;
+  // the token rows streamed: [s0, s1) (SOLO: reset for each run of shards)
+  int64_t s0 = span.s0, s1 = span.s1;
   int64_t s1t[TW];
 #pragma unroll
   for (int i = 0; i < TW; ++i)
     s1t[i] = i >= nq ? s0 : (i == nq - 1 ? s1 : shard_span(a.layout, L, a.T, qt0 + i, a.S_max, a.kvp, a.B, a.Hkv,
                                                             j, b, kvh).s1);
-  const int64_t slab = span.slab;                  // cache block of this shard
+  int64_t slab = span.slab;                        // cache block of this shard
   const int64_t bh = (int64_t)b * a.Hkv + kvh;     // fp8 scales are per (request, KV head)
-  const int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
 
   // The cache arrays are viewed as rows of ROW bytes (scales: kD/32 bytes).
   // Contiguous and sharded layouts: token t of this shard is row
   // slab * S_max + t, so pointers start at the slab; paged: rows come from
   // the block table (phys_row) and pointers start at the pool.
-  const int64_t row0 = PAGED ? 0 : slab * a.S_max;
-  const uint8_t* kdata = static_cast<const uint8_t*>(a.k) + row0 * ROW;
-  const uint8_t* vdata = static_cast<const uint8_t*>(a.v) + row0 * ROW;
+  const uint8_t* kdata = nullptr;
+  const uint8_t* vdata = nullptr;
   const uint8_t* ksdata = nullptr;
   const uint8_t* vsdata = nullptr;
+  auto set_slab = [&](int64_t sl) {
+    slab = sl;
+    const int64_t row0 = PAGED ? 0 : sl * a.S_max;
+    kdata = static_cast<const uint8_t*>(a.k) + row0 * ROW;
+    vdata = static_cast<const uint8_t*>(a.v) + row0 * ROW;
+    if constexpr (KV == kMXFP4) {
+      ksdata = static_cast<const uint8_t*>(a.k_scale) + row0 * (kD / 32);
+      vsdata = static_cast<const uint8_t*>(a.v_scale) + row0 * (kD / 32);
+    }
+  };
+  set_slab(span.slab);
   auto hrow = [&](int64_t t) -> int64_t {
     if constexpr (PAGED) {
       return phys_row(a, b, kvh, slab, t);
@@ -444,10 +505,6 @@ void gqa_mfma_kernel(PartialArgs a) {
   if constexpr (KV == kFP8) {
     kscale = static_cast<const float*>(a.k_scale)[bh];
     vscale = static_cast<const float*>(a.v_scale)[bh];
-  }
-  if constexpr (KV == kMXFP4) {
-    ksdata = static_cast<const uint8_t*>(a.k_scale) + row0 * (kD / 32);
-    vsdata = static_cast<const uint8_t*>(a.v_scale) + row0 * (kD / 32);
   }
   // raw logit -> log2 domain.  A negative fp8 K scale flips the sign of
   // every logit of the slab: the query operands carry that sign, so the raw
@@ -480,7 +537,7 @@ void gqa_mfma_kernel(PartialArgs a) {
     lsum[i] = 0.0f;
   }
 
-  const int64_t last = s1 - 1;
+  int64_t last = s1 - 1;
   // Per-lane byte offsets inside a tile (loop invariant, 32-bit): a full tile
   // is addressed as (wave-uniform tile pointer) + (lane offset) + (immediate),
   // which needs no per-load vector arithmetic.
@@ -749,7 +806,8 @@ void gqa_mfma_kernel(PartialArgs a) {
     }
   };
 
-  const int nfull = (int)((s1 - s0) / kTile);
+  int nfull = (int)((s1 - s0) / kTile);
+  int ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
   if constexpr (LDSRING) {
     static_assert(KV == kBF16, "LDS ring: bf16 cache only");
     using R = Ring;
@@ -844,37 +902,132 @@ void gqa_mfma_kernel(PartialArgs a) {
     }
     __syncthreads();   // every wave is done with its slots before the merge reuses them
   } else {
-    // Stream over this wave's full tiles with kRing register buffers: the loads
-    // of the next kRing-1 tiles are in flight while a tile is computed.  (With
-    // several query tokens a tile takes several times longer to compute, so
-    // one tile ahead is enough and leaves the registers to the tokens.)  The
-    // next loads are always issued (clamped to the last full tile) so the waits
-    // stay static.  A partial last tile is handled once, after the ring.
-    if (nfull > 0) {
-      auto clampt = [&](int t) { return t < nfull - 1 ? t : nfull - 1; };
-      int tile = wave;
-      // rb[k] holds tile wave + (n kRing + k) kWaves; the loop body is
-      // unrolled kRing times so that every buffer index is a constant
-      Raw<KV> rb[kRing];
+    // Stream over this wave's full tiles of [s0, s1) with kRing register
+    // buffers: the loads of the next kRing-1 tiles are in flight while a tile
+    // is computed.  (With several query tokens a tile takes several times
+    // longer to compute, so one tile ahead is enough and leaves the registers
+    // to the tokens.)  The next loads are always issued (clamped to the last
+    // full tile) so the waits stay static.  A partial last tile is handled
+    // once, after the ring.  on_tile(tile) runs before each tile's compute.
+    auto stream_tiles = [&](auto&& on_tile) {
+      if (nfull > 0) {
+        auto clampt = [&](int t) { return t < nfull - 1 ? t : nfull - 1; };
+        int tile = first;
+        // rb[k] holds tile first + (n kRing + k) kStride; the loop body is
+        // unrolled kRing times so that every buffer index is a constant
+        Raw<KV> rb[kRing];
 #pragma unroll
-      for (int k = 0; k < kRing - 1; ++k) load(rb[k], clampt(tile + k * kWaves), FullTile{});
-      bool more = tile < nfull;
-      while (more) {
+        for (int k = 0; k < kRing - 1; ++k) load(rb[k], clampt(tile + k * kStride), FullTile{});
+        bool more = tile < nfull;
+        while (more) {
 #pragma unroll
-        for (int k = 0; k < kRing; ++k) {
-          if (more) {
-            load(rb[(k + kRing - 1) % kRing], clampt(tile + (kRing - 1) * kWaves), FullTile{});
-            compute(rb[k], tile, Unmasked{});
-            tile += kWaves;
-            more = tile < nfull;
+          for (int k = 0; k < kRing; ++k) {
+            if (more) {
+              load(rb[(k + kRing - 1) % kRing], clampt(tile + (kRing - 1) * kStride), FullTile{});
+              on_tile(tile);
+              compute(rb[k], tile, Unmasked{});
+              tile += kStride;
+              more = tile < nfull;
+            }
           }
         }
       }
-    }
-    if (nfull < ntiles && nfull % kWaves == wave) {
-      Raw<KV> rt;
-      load(rt, nfull, PartTile{});
-      compute(rt, nfull, Masked{});
+      if (nfull < ntiles && (SOLO || nfull % kWaves == wave)) {
+        Raw<KV> rt;
+        load(rt, nfull, PartTile{});
+        on_tile(nfull);
+        compute(rt, nfull, Masked{});
+      }
+    };
+    if constexpr (!SOLO) {
+      stream_tiles([](int) {});
+    } else {
+      // ---- one wave per group of shards j .. j1 - 1.  finalize(js) writes
+      // shard js's partial from this wave's state and resets the state.  Lane
+      // (n, g) holds head n, dv = 32g + 8e + blk in acc[0][blk][e], so float4
+      // k of its 32 columns is acc[0][4 (k % 2) + i][k / 2], i < 4.
+      // Finished partials wait in this wave's kStash LDS slots and go out in
+      // one batch of stores at the end (a group has at most kStash shards).
+      extern __shared__ __attribute__((aligned(16))) float stash_lds[];
+      constexpr int kSlots = Layout<KV>::kStash;
+      float* const my_stash = stash_lds + wave * kSlots * kStashFloats;
+      int nstash = 0;
+      uint64_t stash_js = 0;   // shard of slot s in bits [16s, 16s + 16)
+      auto flush = [&]() {
+        for (int sl = 0; sl < nstash; ++sl) {
+          const int js = (int)((stash_js >> (16 * sl)) & 0xFFFFu);
+          const float* src = my_stash + sl * kStashFloats;
+          const int64_t orow = (((int64_t)js * a.B + b) * a.T + qt0) * a.Hq + kvh * 16 + r16;
+          float4* dst = reinterpret_cast<float4*>(a.o_part + orow * kD + 32 * g);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) dst[k] = *reinterpret_cast<const float4*>(src + r16 * kStashRow + 32 * g + 4 * k);
+          if (g == 0) a.lse_part[orow] = src[16 * kStashRow + r16];
+        }
+        nstash = 0;
+        stash_js = 0;
+      };
+      // finalize(js): shard js's partial from this wave's state into the next
+      // stash slot, and the state reset.  Lane (n, g) holds head n,
+      // dv = 32g + 8e + blk in acc[0][blk][e], so float4 k of its 32 columns is
+      // acc[0][4 (k % 2) + i][k / 2], i < 4.
+      auto finalize = [&](int js) {
+        const float lw = rows4_sum(lsum[0]);
+        const bool empty = m2[0] == -INFINITY;
+        const float ln = F16PV ? acc[0][NACC - 1][0] : lw;
+        const float inv = empty ? 0.0f : vscale / ln;
+        float* slot = my_stash + nstash * kStashFloats;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int e = k / 2, b0 = 4 * (k % 2);
+          *reinterpret_cast<float4*>(slot + r16 * kStashRow + 32 * g + 4 * k) =
+              make_float4(acc[0][b0][e] * inv, acc[0][b0 + 1][e] * inv, acc[0][b0 + 2][e] * inv,
+                          acc[0][b0 + 3][e] * inv);
+        }
+        if (g == 0) slot[16 * kStashRow + r16] = empty ? -INFINITY : (m2[0] - POFF + fast_log2(lw)) * kLn2;
+        stash_js |= (uint64_t)js << (16 * nstash);
+        ++nstash;   // at most solo_shards <= kSlots finalizations per wave
+#pragma unroll
+        for (int k = 0; k < NACC; ++k) acc[0][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m2[0] = -INFINITY;
+        lsum[0] = 0.0f;
+      };
+      auto span_of = [&](int js) { return shard_span(a.layout, L, 1, 0, a.S_max, a.kvp, a.B, a.Hkv, js, b, kvh); };
+      const int j1 = j + a.solo_shards < a.kvp ? j + a.solo_shards : a.kvp;
+      // Consecutive shards of a contiguous or paged cache are one run of token
+      // positions, streamed without a break when every shard boundary is a
+      // tile boundary (shard length a multiple of the tile); otherwise, and
+      // for sharded layouts (one slab per shard), shard by shard.
+      bool one_run = a.layout == kContiguous || a.layout == kPaged;
+      if (one_run) {
+        const int64_t Lc = L < 0 ? 0 : (L > a.S_max ? a.S_max : L);
+        const int64_t per = (Lc + a.kvp - 1) / a.kvp;
+        one_run = ((per + 15) / 16 * 16) % kTile == 0;
+      }
+      for (int jj = j; jj < j1;) {
+        const int je = one_run ? j1 : jj + 1;
+        const ShardSpan sa = span_of(jj);
+        s0 = sa.s0;
+        s1 = je == jj + 1 ? sa.s1 : span_of(je - 1).s1;
+        s1t[0] = s1;
+        last = s1 - 1;
+        nfull = (int)((s1 - s0) / kTile);
+        ntiles = (int)((s1 - s0 + kTile - 1) / kTile);
+        set_slab(sa.slab);
+        int jcur = jj;
+        int64_t bound = sa.s1;   // end of shard jcur
+        stream_tiles([&](int tile) {
+          const int64_t base = s0 + (int64_t)tile * kTile;
+          while (base >= bound) {   // the tile starts a later shard
+            finalize(jcur);
+            ++jcur;
+            bound = span_of(jcur).s1;
+          }
+        });
+        for (; jcur < je; ++jcur) finalize(jcur);
+        jj = je;
+      }
+      flush();
+      return;
     }
   }
   // ---- merge the four waves' states of each token and write its partial
@@ -953,12 +1106,40 @@ int tokens_per_workgroup(int T, int kv) {
   return (kv == kBF16 && T >= 3) ? 4 : 2;
 }
 
+// Shards per wave for the one-wave split (0: the four-wave split): from
+// Layout::kSoloWaves shard units on, each wave streams units / kSoloWaves
+// consecutive shards, at least one and at most the kStash its LDS slots hold,
+// so the pass runs about kSoloWaves long streams.
+template <int KV>
+int solo_shards(int64_t units) {
+  constexpr int64_t W = Layout<KV>::kSoloWaves;
+  if (W == 0 || units < W) return 0;
+  const int64_t n = units / W;
+  return (int)(n < Layout<KV>::kStash ? n : Layout<KV>::kStash);
+}
+
+// A one-token instance, with the format's dynamic LDS: the partials stash of
+// the one-wave groups, or the reservation that sets the occupancy.
+template <int KV, bool PAGED, bool SOLO>
+hipError_t launch_one_token(const PartialArgs& a, dim3 grid, hipStream_t stream) {
+  auto fn = gqa_mfma_kernel<KV, PAGED, true, 1, false, SOLO>;
+  const size_t lds = SOLO ? stash_bytes<KV>() : (size_t)Layout<KV>::kLdsReserve;
+  static_assert(stash_bytes<KV>() <= 160 * 1024, "stash fits the LDS");
+  if (lds > 64 * 1024) {
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, stream, a);
+  return hipSuccess;
+}
+
 // The four-token instance (bf16 cache, LDS ring of tiles) with NT loads or not.
 template <int KV, bool PAGED, bool NT>
 hipError_t launch_gqa_ring(const PartialArgs& a, dim3 grid, hipStream_t stream) {
   constexpr size_t kLds = (size_t)kWaves * Ring::kWaveBytes;
   static_assert(kLds >= sizeof(MergeLds) && kLds <= 160 * 1024, "LDS ring budget");
-  auto fn = gqa_mfma_kernel<KV, PAGED, NT, 4, true>;
+  auto fn = gqa_mfma_kernel<KV, PAGED, NT, 4, true, false>;
   // more than 64 KB of dynamic LDS: raise the kernel's limit once (the
   // initialization of a local static is thread-safe)
   static const hipError_t attr =
@@ -977,13 +1158,20 @@ hipError_t launch_gqa3(const PartialArgs& a, hipStream_t stream) {
   const int nchunks = (a.T + tw - 1) / tw;
   const int64_t blocks = unit_token_blocks((int64_t)a.kvp * a.B * a.Hkv, nchunks);
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (tw == 1) {
-    hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, true, 1, false>), grid, block, 0, stream, a);
+  const int64_t units = (int64_t)a.kvp * a.B * a.Hkv;
+  const int nsh = tw == 1 ? solo_shards<KV>(units) : 0;
+  if (nsh > 0) {
+    PartialArgs as = a;
+    as.solo_shards = nsh;
+    const int64_t groups = (int64_t)((a.kvp + nsh - 1) / nsh) * a.B * a.Hkv;
+    return launch_one_token<KV, PAGED, true>(as, dim3((unsigned)((groups + kWaves - 1) / kWaves)), stream);
+  } else if (tw == 1) {
+    return launch_one_token<KV, PAGED, false>(a, grid, stream);
   } else if (tw == 2) {
     if (nchunks == 1)
-      hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, true, 2, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, true, 2, false, false>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, false, 2, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gqa_mfma_kernel<KV, PAGED, false, 2, false, false>), grid, block, 0, stream, a);
   } else if constexpr (KV == kBF16) {
     return nchunks == 1 ? launch_gqa_ring<KV, PAGED, true>(a, grid, stream)
                         : launch_gqa_ring<KV, PAGED, false>(a, grid, stream);

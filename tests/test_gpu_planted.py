@@ -247,3 +247,23 @@ def test_fp8_negative_and_zero_scales(shape, T):
     q = np.ascontiguousarray(inp.q.reshape(w.B, T, w.Hq, w.Dqk))
     for kvp in (1, 4, 32):
         _check_inputs(w, inp, q, "contiguous", kvp, [(300, 77, 5)])
+
+
+# ------------------------------------------------------- many shard units
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("S", [2048, 8192])
+def test_one_wave_shard_groups(kv, layout, S):
+    """From 1024 (fp8) or 2048 (MXFP4) shard units on, the one-token GQA kernel
+    gives each wave a group of consecutive shards of one (request, KV head):
+    when every shard length of the request is a multiple of the 32-token tile
+    the group is streamed as one run of tokens with each shard's partial
+    written at its boundary, otherwise shard by shard.  S = 2048 gives
+    16-token shards (shard by shard), S = 8192 runs of 32- and 64-token
+    shards next to 16-token ones; with empty shards, an empty request and
+    groups cut short by kvp."""
+    w = _wl(kv, 1, B=4, Hq=8 * 16, Hkv=8, S=S, seq=(S, S - 49, 37, 0), seed=71)
+    inp = kvgen.make_inputs(w)
+    q = np.ascontiguousarray(inp.q.reshape(w.B, 1, w.Hq, w.Dqk))
+    for kvp in (128, 200, 256):
+        _check_inputs(w, inp, q, layout, kvp, [(S, S - 49, 37, 0), (S // 2, S, 0, 33)])
