@@ -246,6 +246,10 @@ WORKLOADS = {
     "helix_shard_mxfp4": Workload("helix_shard_mxfp4", B=8, Hq=16, Hkv=1, Dqk=128, Dv=128,
                                   S_max=1 << 17, kvp=(64, 16, 128), q_dtype="bf16",
                                   kv_dtype="mxfp4", seed=1007),
+    # A group of 8 query heads per KV head at the Helix length: B=8, 64/8 heads,
+    # Hsz=128, S=2^20, fp8 E4M3 cache.
+    "gqa8_fp8": Workload("gqa8_fp8", B=8, Hq=64, Hkv=8, Dqk=128, Dv=128, S_max=1 << 20,
+                         kvp=(32, 8, 128), q_dtype="bf16", kv_dtype="fp8", seed=1008),
     # MLA-style: 128 query heads on one 576-wide latent head; V = first 512 dims of K.
     "mla_bf16": Workload("mla_bf16", B=8, Hq=128, Hkv=1, Dqk=576, Dv=512, S_max=1 << 19,
                          kvp=(32,), q_dtype="bf16", kv_dtype="bf16", seed=1005,

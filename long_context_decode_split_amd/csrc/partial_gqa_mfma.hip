@@ -513,15 +513,21 @@ void gqa_mfma_kernel(PartialArgs a) {
   const uint32_t qsign = kscale < 0.0f ? 0x80008000u : 0u;
 
   // Q^T operands of each token of the chunk (a token past the end of T loads
-  // the last one's): lane (n, g) holds head n, the 8 dims chunk_d(c, g).
+  // the last one's): lane (n, g) holds head n, the 8 dims chunk_d(c, g).  A
+  // group of G < 16 heads fills the first G of the 16 MFMA columns; the other
+  // columns get zero queries and their outputs are never written.
+  const int G = a.Hq / a.Hkv;
+  const bool head_ok = r16 < G;
   bf16x8_t qop[TW][4];
 #pragma unroll
   for (int i = 0; i < TW; ++i) {
     const int qt = qt0 + (i < nq ? i : nq - 1);
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.T + qt) * a.Hq + kvh * 16 + r16) * kD;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.T + qt) * a.Hq + kvh * G + (head_ok ? r16 : 0)) * kD;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + Lay::chunk_d(c, g));
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + Lay::chunk_d(c, g));
+      if (!head_ok) v = make_uint4(0u, 0u, 0u, 0u);
       qop[i][c] = as_bf16x8(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
     }
   }
@@ -957,7 +963,8 @@ void gqa_mfma_kernel(PartialArgs a) {
         for (int sl = 0; sl < nstash; ++sl) {
           const int js = (int)((stash_js >> (16 * sl)) & 0xFFFFu);
           const float* src = my_stash + sl * kStashFloats;
-          const int64_t orow = (((int64_t)js * a.B + b) * a.T + qt0) * a.Hq + kvh * 16 + r16;
+          if (!head_ok) continue;
+          const int64_t orow = (((int64_t)js * a.B + b) * a.T + qt0) * a.Hq + kvh * G + r16;
           float4* dst = reinterpret_cast<float4*>(a.o_part + orow * kD + 32 * g);
 #pragma unroll
           for (int k = 0; k < 8; ++k) dst[k] = *reinterpret_cast<const float4*>(src + r16 * kStashRow + 32 * g + 4 * k);
@@ -1049,9 +1056,9 @@ void gqa_mfma_kernel(PartialArgs a) {
       mrg->ln[wave][r16] = F16PV ? acc[i][NACC - 1][0] : lw;
     }
     __syncthreads();
-    const int64_t orow0 = (((int64_t)j * a.B + b) * a.T + qt0 + i) * a.Hq + kvh * 16;   // o_part / lse_part row
+    const int64_t orow0 = (((int64_t)j * a.B + b) * a.T + qt0 + i) * a.Hq + kvh * G;   // o_part / lse_part row
     const int tid = threadIdx.x;
-    for (int idx = tid; idx < 16 * kD; idx += kThreads) {
+    for (int idx = tid; idx < G * kD; idx += kThreads) {
       const int n = idx / kD;
       const int d = idx - n * kD;
       float M = mrg->m[0][n];
@@ -1070,7 +1077,7 @@ void gqa_mfma_kernel(PartialArgs a) {
       }
       a.o_part[(orow0 + n) * kD + d] = o;
     }
-    if (tid < 16) {
+    if (tid < G) {
       float M = mrg->m[0][tid];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg->m[w][tid]);
@@ -1091,7 +1098,9 @@ void gqa_mfma_kernel(PartialArgs a) {
 bool gqa_mfma_supports(const PartialArgs& a) {
   if (!a.q_bf16 || a.v_aliases_k) return false;
   if (a.Dqk != kD || a.Dv != kD) return false;
-  if (a.Hq / a.Hkv != 16) return false;
+  // groups of up to 16 query heads (fewer fill part of the 16 MFMA columns)
+  const int G = a.Hq / a.Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
   return a.kv_format == kBF16 || a.kv_format == kFP8 || a.kv_format == kMXFP4;
 }
 

@@ -335,6 +335,15 @@ def test_full_helix_mxfp4(kvp):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("kvp", [32, 128])
+def test_full_gqa8_fp8(kvp):
+    """Eight query heads per KV head at S = 2^20 (fp8): the matrix-core kernel
+    with half of its 16 head columns padded."""
+    _check_sampled("gqa8_fp8", kvp, n_pairs=2)
+    _check_peaked("gqa8_fp8", kvp)
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("name", ["mxfp4_b1_s256k", "mxfp4_b32_s256k"])
 def test_full_mxfp4_batch_sweep(name):
     _check_sampled(name, 32, n_pairs=2)

@@ -125,6 +125,16 @@ def test_rising_logits_gqa(kv, T, layout):
     _check_inputs(w, inp, q, layout, 1, [(700, 61)])
 
 
+@pytest.mark.parametrize("kv,G", [("fp8", 8), ("mxfp4", 4), ("bf16", 1)])
+@pytest.mark.parametrize("T", [1, 2])
+def test_rising_logits_small_groups(kv, G, T):
+    """Groups of fewer than 16 query heads on the matrix-core kernel (padded
+    head columns): rising logits, contiguous cache."""
+    w = _wl(kv, T, Hq=2 * G, Hkv=2)
+    inp, q = _ramp(w, 0.3)
+    _check_inputs(w, inp, q, "contiguous", 4, [(700, 333)])
+
+
 @pytest.mark.parametrize("T", [1, 2])
 def test_rising_logits_latent(T):
     """The latent kernel's restart pass (a later tile beyond its first tile's
