@@ -54,19 +54,20 @@ MFMA_BUSY = {
     ("helix_mxfp4", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 0.3513,
     ("helix_fp8", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 0.1730,
 }
-KERNEL_SOURCES = {"bf16": "partial_gqa_mfma.hip", "fp8": "partial_gqa_mfma.hip",
-                  "mxfp4": "partial_gqa_mfma.hip", "f32": "partial_valu.hip"}
+_GQA_SOURCES = ("partial_gqa_mfma.hip", "gqa_mfma_kernel.hpp", "partial_gqa_mfma_tokens.hip")
+KERNEL_SOURCES = {"bf16": _GQA_SOURCES, "fp8": _GQA_SOURCES, "mxfp4": _GQA_SOURCES,
+                  "f32": ("partial_valu.hip",), "latent": ("partial_mla_mfma.hip",)}
 
 
 def kernel_hash(kv_dtype, mla=False):
-    """sha256 prefix of the partial kernel's code (its source file plus the
+    """sha256 prefix of the partial kernel's code (its source files plus the
     shared device header), with // comments and blank space removed, so that
     comment edits keep the recorded counters."""
     import hashlib
     import re
-    name = "partial_mla_mfma.hip" if mla else KERNEL_SOURCES[kv_dtype]
+    names = KERNEL_SOURCES["latent" if mla else kv_dtype]
     h = hashlib.sha256()
-    for f in (name, "kvd_device.hpp"):
+    for f in names + ("kvd_device.hpp",):
         with open(os.path.join(HERE, "long_context_decode_split_amd", "csrc", f)) as fh:
             code = re.sub(r"//[^\n]*", "", fh.read())
         h.update(" ".join(code.split()).encode())
@@ -135,20 +136,24 @@ def cpu_baseline(w, target_s=15.0):
 
 
 # How each kernel family computes, for the bench line (keyed by kv format;
-# "latent" for the 576/512 latent-head kernel).
+# "latent" for the 576/512 latent-head kernel), and the arithmetic types of
+# its products ("dtype").
 ARITH = {
     "f32": "fp32 vector ALU: logits, softmax and P.V in fp32",
     "bf16": "bf16 MFMA logits (16x16x32) on the bf16 cache; P.V on bf16 MFMA with P as a bf16 hi+lo pair; "
             "fp32 accumulation and softmax",
-    "fp8": "block-scaled f8f6f4 MFMA logits on the raw E4M3 K bytes with the bf16 query as two E4M3 parts "
-           "(unit block scales, the fp32 slab scale folded into the log2 multiplier); V decoded to bf16, P.V on "
-           "bf16 MFMA with P as a bf16 hi+lo pair; fp32 accumulation and softmax",
-    "mxfp4": "block-scaled f8f6f4 MFMA logits on the raw E2M1 K nibbles with their E8M0 block exponents and the "
-             "bf16 query as two E4M3 parts; V decoded to bf16 with its block scales, P.V on bf16 MFMA with P as a "
-             "bf16 hi+lo pair; fp32 accumulation and softmax",
+    "fp8": "bf16 MFMA logits (16x16x32) on K decoded exactly from E4M3 (the fp32 slab scale folded into the "
+           "log2 multiplier); V decoded exactly to fp16, P.V on fp16 MFMA with P = 2^(s - m + 7) rounded to "
+           "fp16 and normalized by the sum of those fp16 weights (one more MFMA); fp32 accumulation, softmax "
+           "and log-sum-exp",
+    "mxfp4": "bf16 MFMA logits (16x16x32) on K decoded exactly from E2M1 with its E8M0 block exponents; V "
+             "decoded exactly to fp16 with its block scales, P.V on fp16 MFMA with P = 2^(s - m + 7) rounded to "
+             "fp16 and normalized by the sum of those fp16 weights (tiles whose V exponents leave fp16's range: "
+             "bf16 V against P as a bf16 hi+lo pair); fp32 accumulation, softmax and log-sum-exp",
     "latent": "bf16 MFMA logits over the 576-wide latent rows and P.V over their first 512 columns (P as a bf16 "
               "hi+lo pair), tiles staged through an LDS ring; fp32 accumulation and softmax",
 }
+DTYPE = {"f32": "f32", "bf16": "bf16", "fp8": "bf16+fp16", "mxfp4": "bf16+fp16", "latent": "bf16"}
 # Executed P.V flops per algorithmic ones on the latent kernel (P as a bf16
 # hi+lo pair runs the product twice).
 LATENT_PV_PASSES = 2
@@ -267,7 +272,7 @@ def measure(args, name, kvp_req, T, layout, block_len, timing_extras=True):
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "hbm_peak_frac": round(value / peak, 4),
-        "dtype": w.kv_dtype,
+        "dtype": DTYPE[fam],
         "arith": ARITH[fam],
         "config": {"workload": w.name, "layout": layout,
                    "block_len": block_len if layout == "paged" else None, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,

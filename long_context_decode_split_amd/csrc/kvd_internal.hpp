@@ -67,6 +67,10 @@ hipError_t launch_partial_valu(const PartialArgs& a, hipStream_t stream);
 bool gqa_mfma_supports(const PartialArgs& a);
 hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream);
 
+// One-wave GQA instances for 2 <= T <= 4 query tokens of an fp8 or MXFP4
+// cache, one (shard, two-token chunk) per wave (partial_gqa_mfma_tokens.hip).
+hipError_t launch_gqa_solo_tokens(const PartialArgs& a, hipStream_t stream);
+
 bool mla_mfma_supports(const PartialArgs& a);
 hipError_t launch_partial_mla_mfma(const PartialArgs& a, hipStream_t stream);
 

@@ -3,7 +3,8 @@
 * Logits that rise along the sequence, so every kernel instance moves its
   running max past the first tile: the one-token matrix-core GQA kernel on
   bf16, fp8 and MXFP4 caches; its two-token register ring (fp8, MXFP4, bf16
-  T = 2) with one and with several token chunks; the four-token LDS ring of
+  T = 2) with one and with several token chunks; the one-wave two-token
+  chunks of fp8 and MXFP4 caches (T = 2 to 4); the four-token LDS ring of
   the bf16 cache; the latent kernel and the vector-ALU kernel; contiguous
   and paged caches.
 * MXFP4 block exponents far from 127 in K and in V, and all-zero blocks at
@@ -277,3 +278,23 @@ def test_one_wave_shard_groups(kv, layout, S):
     q = np.ascontiguousarray(inp.q.reshape(w.B, 1, w.Hq, w.Dqk))
     for kvp in (128, 200, 256):
         _check_inputs(w, inp, q, layout, kvp, [(S, S - 49, 37, 0), (S // 2, S, 0, 33)])
+
+
+# fp8 from 1024 shard units on (4 requests x 8 KV heads x kvp 64 / 100 at
+# S = 4096: 64- and 48-token shards), MXFP4 from 8192 (kvp 256 / 300 at
+# S = 16384: 64-token shards)
+TOKEN_CHUNK_CASES = [("fp8", lay, T) for lay in ("contiguous", "paged") for T in (2, 3, 4)] + [
+    ("mxfp4", "contiguous", 2), ("mxfp4", "paged", 3), ("mxfp4", "contiguous", 4)]
+
+
+@pytest.mark.parametrize("kv,layout,T", TOKEN_CHUNK_CASES, ids=lambda x: str(x))
+def test_one_wave_token_chunks(kv, layout, T):
+    """With enough shard units, two to four query tokens of an fp8 or MXFP4
+    cache run one wave per (shard, chunk of two tokens), the chunks of a shard
+    in one workgroup.  Rising logits (the running max of every token moves at
+    every tile), ragged and empty shards, an empty request."""
+    S, kvps = (4096, (64, 100)) if kv == "fp8" else (16384, (256, 300))
+    w = _wl(kv, T, B=4, Hq=8 * 16, Hkv=8, S=S, seq=(S, S - 49, 37, 0), seed=73)
+    inp, q = _ramp(w, 0.3, seed=9)
+    for kvp in kvps:
+        _check_inputs(w, inp, q, layout, kvp, [(S, S - 49, 37, 0)])
