@@ -150,13 +150,15 @@ ARITH = {
              "decoded exactly to fp16 with its block scales, P.V on fp16 MFMA with P = 2^(s - m + 7) rounded to "
              "fp16 and normalized by the sum of those fp16 weights (tiles whose V exponents leave fp16's range: "
              "bf16 V against P as a bf16 hi+lo pair); fp32 accumulation, softmax and log-sum-exp",
-    "latent": "bf16 MFMA logits over the 576-wide latent rows and P.V over their first 512 columns (P as a bf16 "
-              "hi+lo pair), tiles staged through an LDS ring; fp32 accumulation and softmax",
+    "latent": "bf16 MFMA logits (32x32x16) over the 576-wide latent rows; P.V over their first 512 columns on "
+              "fp16 MFMA (32x32x16) with V converted exactly from bf16 and P = 2^(s - m + 7) rounded to fp16, "
+              "normalized by the sum of those fp16 weights; tiles staged through an LDS ring, the weights "
+              "exchanged between the 4 waves through LDS; fp32 accumulation, softmax and log-sum-exp",
 }
-DTYPE = {"f32": "f32", "bf16": "bf16", "fp8": "bf16+fp16", "mxfp4": "bf16+fp16", "latent": "bf16"}
-# Executed P.V flops per algorithmic ones on the latent kernel (P as a bf16
-# hi+lo pair runs the product twice).
-LATENT_PV_PASSES = 2
+DTYPE = {"f32": "f32", "bf16": "bf16", "fp8": "bf16+fp16", "mxfp4": "bf16+fp16", "latent": "bf16+fp16"}
+# Executed P.V flops per algorithmic ones on the latent kernel (one fp16
+# product).
+LATENT_PV_PASSES = 1
 
 # Workloads measured next to the headline by a default run (the MXFP4 Helix
 # shape and the latent-head shape, both at kvp = 32).

@@ -4,39 +4,35 @@
 // 64 rotary dims); V is the first 512 columns of the same row, so each cached
 // byte is read from HBM once and serves both products:
 //
-//   S^T[token, head] = K_tile[token, 0:576] . Q[head, 0:576]   (18 MFMAs / 16x16 block)
+//   S^T[token, head] = K_tile[token, 0:576] . Q[head, 0:576]
 //   O^T[dv, head]   += K_tile[token, 0:512]^T . P^T[token, head]
 //
-// both on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; P enters the PV
-// product as a bf16 hi + lo pair (two MFMAs), as in the GQA kernel.  The
-// accumulator (256 AGPRs per wave) is never rescaled: see the pass structure
-// below.
+// both on 32x32x16 MFMAs with fp32 accumulation: the logits on bf16, the PV
+// product on fp16, with V converted from bf16 (exact below 2^16) and the
+// weights P = 2^(logit - reference max + 7) rounded to fp16, the output
+// normalized by the sum of those fp16 weights.  (The 32x32 MFMAs let the
+// vector ALU work of a wave proceed under them, where 16x16 ones stall it for
+// part of each instruction.)  The accumulator (256 AGPRs per wave) is never
+// rescaled: see the pass structure below.
 //
 // Work split: one workgroup of 4 waves per (shard j, request b, KV head, query
-// token; a single-token decode has one).  The
-// shard is walked in 32-token tiles shared by all four waves; wave w owns heads
-// 32w .. 32w+31, keeping their Q (144 VGPRs) and their O^T accumulator (32 heads
-// x 512 dv, 256 AGPRs) in registers for the whole shard; LDS traffic per
-// cached token is 4 x (1152 + 1024) bytes.
+// token; a single-token decode has one).  The shard is walked in 32-token
+// tiles shared by all four waves.  Wave w computes the logits and weights of
+// heads 32w .. 32w+31 (their Q, 144 VGPRs, stays in registers), the four
+// waves exchange the fp16 weights through LDS, and wave w then accumulates
+// value columns 128w .. 128w+127 of all 128 heads (256 AGPRs).  Per tile a
+// wave reads the whole K tile for its logits and only its quarter of V.
 //
 // Tiles travel HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a
 // ring of kBufs buffers, kAhead = 3 tiles ahead.  A buffer has two regions: the first
 // 1024 bytes of each of the 32 rows (dims 0..511) at a stride of 65 16-byte
 // slots, one row per load instruction, and the last 128 bytes (dims 512..575)
 // at a stride of 9 slots, four rows per load instruction.  Every source
-// address is a wave-uniform row pointer plus a fixed lane offset.
-//
-// Within each 16-token half-tile, MFMA row m holds token perm16(m), which
-// interleaves even and odd tokens so that, in a model of 32 four-byte LDS
-// banks, the 8 rows read together by a ds_read_b128 of K fall on 8 different
-// 16-byte bank groups (strides 65 and 9 are 1 mod 8) and the four rows read
-// by each 16-lane ds_read_b64_tr_b16 group of V are 8 banks apart.  (Measured
-// on gfx950, these strided reads still cost about 8 clocks per b128 and per
-// tr16 instruction, against about 6 for a lane-contiguous b128.)  K operands
-// are ds_read_b128 of 8 contiguous dims of one token; V^T operands come from
-// ds_read_b64_tr_b16, whose 16-lane transpose turns four 16-column row
-// segments into one column of 4 tokens per lane, which is exactly the V^T
-// MFMA operand.
+// address is a wave-uniform row pointer plus a fixed lane offset.  The odd
+// row strides put the 16 rows a 16-lane group of a ds_read_b128 of K reads
+// (one 16-byte slot each) on 16 different slots of the banks.  V^T operands
+// come from ds_read_b64_tr_b16, whose 16-lane transpose turns four
+// 16-column row segments into one column of 4 tokens per lane.
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
 
@@ -44,7 +40,11 @@ namespace kvd {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __fp16 h16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -67,7 +67,13 @@ constexpr int kBufBytes = kMainBytes + kTailBytes;     // 37888
 constexpr int kBufs = 4;
 constexpr int kAhead = kBufs - 1;           // tiles in flight ahead of the one computed
 constexpr int kLoads = kRowsPerWave + kRowsPerWave / 4;  // load instructions per wave per tile
-constexpr float kHeadroom = 64.0f;  // max log2 growth of P over the reference
+constexpr int kKAhead = 2;                 // K operand reads in flight ahead of the logits MFMAs
+constexpr int kPBytes = 8 * 64 * 16;        // fp16 weights of one tile, all 128 heads
+// The fp16 weights are 2^kPOffset times exp2(logit - reference max): at most
+// 2^(kPOffset + kHeadroom) = 2^15 < 65504 while no logit exceeds the
+// reference by more than kHeadroom (log2 units), and 2^kPOffset at the max.
+constexpr float kPOffset = 7.0f;
+constexpr float kHeadroom = 8.0f;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4_t v = {a, b, c, d};
@@ -82,9 +88,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
 
 static_assert(2 * kLoads < 64, "vmcnt range");
 
-// Token (within a 16-token half-tile) held by MFMA row m = 4a + i:
-// a = 0 -> 0,2,4,6; a = 1 -> 1,3,5,7; a = 2 -> 8,..,14; a = 3 -> 9,..,15.
-__device__ __forceinline__ int perm16(int m) { return ((m >> 2) & 1) + 2 * (m & 3) + 8 * (m >> 3); }
+
+// The logits MFMA with its accumulator in VGPRs.  The 256 AGPRs of a wave
+// hold its PV accumulator, and the compiler gives every MFMA of a kernel the
+// same (AGPR) form, so these are written out: acc (+)= K Q^T (first: acc =
+// K Q^T).  The compiler does not see an MFMA here, so each block carries the
+// hazard padding it would insert itself: 2 wait states between a vector-ALU
+// write of an operand and the MFMA (s_nop 1), none between MFMAs chained on
+// the same accumulator, and 12 before a vector-ALU read of the result
+// (logit_mfma_drain, s_nop 15: 16).
+__device__ __forceinline__ void logit_mfma(f32x16_t& acc, const uint4& k, const bf16x8_t& q, bool first) {
+  const u32x4_t kv = u32x4_t{k.x, k.y, k.z, k.w};
+  const u32x4_t qv = __builtin_bit_cast(u32x4_t, q);
+  if (first)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(kv), "v"(qv));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kv), "v"(qv));
+}
+__device__ __forceinline__ void logit_mfma_drain() { asm volatile("s_nop 15" ::: "memory"); }
 
 // PAGED: rows are found through the block table (paged cache layout).
 template <bool PAGED>
@@ -94,8 +115,8 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   const int lane = threadIdx.x & 63;
   // wave index as a scalar, so everything derived from it stays wave-uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
+  const int l32 = lane & 31;   // row / column of the 32x32 MFMA operands and results
+  const int h2 = lane >> 5;    // which half of the 16-deep k block (operands) or 4-row groups (results)
 
   // unit (shard j, request b, KV head kvh) and query token qt
   int64_t unit;
@@ -126,17 +147,15 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   const float c2 = a.scale_log2;
   const int head0 = kvh * kHeads + wave * 32;
 
-  // Q^T operands: [head block][18 chunks of 32 dims]; lane (n, g) holds head
-  // 16*hb + n, dims 32c + 8g .. 32c + 8g + 7.
-  bf16x8_t qop[2][18];
+  // Q^T operands of the 32x32x16 logits MFMAs: 36 chunks of 16 dims; lane l
+  // holds head head0 + l % 32, dims 16 c + 8 (l / 32) .. +7 of chunk c.
+  bf16x8_t qop[36];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (qrow0 + head0 + l32) * kDqk + 8 * h2;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + (qrow0 + head0 + 16 * hb + r16) * kDqk;
-#pragma unroll
-    for (int c = 0; c < 18; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g);
-      qop[hb][c] = as_bf16x8(v.x, v.y, v.z, v.w);
+    for (int c = 0; c < 36; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * c);
+      qop[c] = as_bf16x8(v.x, v.y, v.z, v.w);
     }
   }
   // Q is in registers before any cache load is issued, so the only vector
@@ -203,196 +222,287 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
     }
   };
 
-  // Per-lane LDS read offsets within a buffer.
-  const int pk = perm16(r16);                  // token of this lane's K operand row
-  const uint32_t k_main = (uint32_t)((pk * kMainStride + g) * 16);
-  const uint32_t k_tail = (uint32_t)(kMainBytes + (pk * kTailStride + g) * 16);
-  const int rr = r16 >> 2;                     // row of the lane's 4x16 transpose group
-  const int q = r16 & 3;                       // 4-column piece of the 16 columns
-  const uint32_t v_off =
-      (uint32_t)((perm16(4 * g + rr) * kMainStride + (q >> 1)) * 16 + (q & 1) * 8);
-  // token (within the tile) of each of the lane's 8 logits, for masking
-  int tok[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) tok[e] = 16 * (e >> 2) + perm16(4 * g + (e & 3));
+  // Per-lane LDS read offsets within a buffer.  K operand of chunk c: row
+  // (token) l32, dims 16 c + 8 h2 .. +7: 16-byte slot 2 c + h2 of the row's
+  // main region (c < 32) or 2 (c - 32) + h2 of its rotary region.
+  const uint32_t k_main = (uint32_t)((l32 * kMainStride + h2) * 16);
+  const uint32_t k_tail = (uint32_t)(kMainBytes + (l32 * kTailStride + h2) * 16);
+  // V^T operand of 32 value columns and 16 tokens (step s of the tile): two
+  // ds_read_b64_tr_b16, jj = 0, 1.  In 16-lane group G = lane / 16, lane
+  // i = lane % 16 addresses row 16 s + 8 jj + 4 (G / 2) + i / 4, columns
+  // 16 (G % 2) + 4 (i % 4) .. +3 of the block; the transpose hands lane i
+  // column 16 (G % 2) + i = l32 of those four rows, which are k = 8 h2 +
+  // 4 jj + 0..3 of the operand: token 16 s + 8 jj + 4 h2 + (k % 4).
+  const int vg = lane >> 4, vi = lane & 15;
+  const uint32_t v_off = (uint32_t)(((4 * (vg >> 1) + (vi >> 2)) * kMainStride) * 16 + 2 * (16 * (vg & 1) + 4 * (vi & 3)));
+  // Result element e of a 32x32 block sits at row 8 (e / 4) + 4 h2 + e % 4,
+  // column l32: logits of token 8 (e / 4) + 4 h2 + e % 4 for head l32, so
+  // the PV step s takes elements 8 s .. 8 s + 7 as its P^T operand (tokens
+  // 16 s + 8 jj + 4 h2 + i at k = 8 h2 + 4 jj + i, as in V^T).
 
-  f32x4_t acc[2][32];
-  float m2[2], lsum[2];
+  // This wave's share of the PV product: value columns 128 wave .. +127 of
+  // all 128 heads; acc[d][H] holds O^T rows 128 wave + 32 d .. +31, heads
+  // 32 H .. 32 H + 31.
+  f32x16_t acc[4][4];
+  // Softmax state of this wave's head head0 + l32 (both halves of the wave
+  // hold the same): reference max (log2 domain), exact fp32 sum of the
+  // weights and sum of the fp16 weights (over this lane's tokens).
+  float m2 = -INFINITY, lsum = 0.f, lsum16 = 0.f;
+  // The fp16 weights of all 128 heads for the current tile: head block H,
+  // step s, lane l at ((2 H + s) 64 + l) 16 bytes (the P^T operand).
+  const uint32_t p_lds = lds0 + (uint32_t)(kBufs * kBufBytes);
+  float* const sum_lds = reinterpret_cast<float*>(smem + kBufs * kBufBytes);   // reused after the passes
+  auto half_max = [](float v) {
+    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+  };
+  auto half_sum = [](float v) {
+    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  };
 
   // Pass structure.  The accumulating pass fixes each head's reference max
-  // at its first tile and never rescales the accumulator; weights may grow to
-  // 2^kHeadroom before that is unsafe.  If any tile of the shard exceeds its
-  // reference by more than kHeadroom (in log2 units) the workgroup reruns the
+  // at its first tile and never rescales the accumulator; the fp16 weights
+  // 2^(x c2 - m + kPOffset) stay below 2^15 while no tile exceeds its
+  // reference by more than kHeadroom.  If one does, the workgroup reruns the
   // shard: a logits-only pass finds each head's exact max, then the
-  // accumulating pass runs again with that max as the reference.
-  bool max_only = false;
-  m2[0] = m2[1] = -INFINITY;
-  for (;;) {
-    if (!max_only) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        lsum[hb] = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < 32; ++blk) acc[hb][blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+  // accumulating pass runs again with that max as the reference.  V enters
+  // the PV product as fp16, exact for bf16 values below 2^16 in magnitude; if
+  // a wave's columns hold a larger one, the shard is rerun with that wave's V
+  // scaled by a power of two (vsc) that brings them into fp16's range, and
+  // the wave's output scaled back.
+  // Wait for tile `tile` (at most the loads of the two tiles issued after it
+  // still in flight), meet the other waves (its loads have landed for all of
+  // them, and all are done with the previous tile: its buffer and the
+  // weights in LDS), issue the loads kAhead tiles on; returns the tile's
+  // valid rows (kTile or more except at the end).
+  auto tile_ready = [&](int tile) {
+    const int after = ntiles - 1 - tile;
+    if (after >= 2) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoads));
+    } else if (after == 1) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
+    __builtin_amdgcn_s_barrier();
+    if (tile + kAhead < ntiles) issue(tile + kAhead, (tile + kAhead) % kBufs);
+    return (int)(s1 - (s0 + (int64_t)tile * kTile));
+  };
+  // Logits S^T[token, head] of the tile in buffer tb for its 32 tokens and
+  // this wave's 32 heads: 36 chunks of 16 dims, K operands read kKAhead
+  // chunks ahead (an LDS read under load takes longer than the 32-cycle
+  // MFMA).  Element e: token 8 (e / 4) + 4 h2 + e % 4, head l32.
+  auto tile_logits = [&](const uint8_t* tb, f32x16_t& sl) {
+    auto kread = [&](int c) {
+      const uint8_t* p = c < 32 ? tb + k_main + 32 * c : tb + k_tail + 32 * (c - 32);
+      return *reinterpret_cast<const uint4*>(p);
+    };
+    // two accumulation chains (chunks 0..17 and 18..35), interleaved so that
+    // no MFMA waits on the one just before it
+    f32x16_t sl2;
+    uint4 kq[kKAhead];
+#pragma unroll
+    for (int i = 0; i < kKAhead; ++i) kq[i] = kread((i & 1) * 18 + (i >> 1));
+#pragma unroll
+    for (int i = 0; i < 36; ++i) {
+      const int c = (i & 1) * 18 + (i >> 1);     // chunk of step i
+      const uint4 k0 = kq[i % kKAhead];
+      if (i + kKAhead < 36) kq[i % kKAhead] = kread(((i + kKAhead) & 1) * 18 + ((i + kKAhead) >> 1));
+      if (i & 1)
+        logit_mfma(sl2, k0, qop[c], i == 1);
+      else
+        logit_mfma(sl, k0, qop[c], i == 0);
+    }
+    logit_mfma_drain();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sl[e] += sl2[e];
+  };
+  // The tile's max logit of head l32 (tokens below nvalid), log2 domain.
+  auto tile_max2 = [&](const f32x16_t& sl, int nvalid) {
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      tmax = fmaxf(tmax, (nvalid >= kTile || 8 * (e >> 2) + 4 * h2 + (e & 3) < nvalid) ? sl[e] : -INFINITY);
+    return half_max(tmax) * c2;
+  };
+
+  bool max_only = false;
+  float vsc = 1.0f;            // scale of this wave's V in the PV product
+  bool vscaled = false;        // vsc != 1 (wave-uniform)
+  float vmax = 0.0f;           // largest |V| this lane has converted
+  for (;;) {
+    // every pass starts from zero (so no pass carries the accumulator into
+    // the next one)
+    lsum = lsum16 = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int H = 0; H < 4; ++H)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[d][H][e] = 0.f;
     int overflow = 0;
 #pragma unroll
     for (int t = 0; t < kAhead; ++t)
       if (t < ntiles) issue(t, t);
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int buf = tile % kBufs;
-      // this tile's loads are done once at most those of the tiles after it
-      // remain in flight (s_waitcnt simm16 on gfx9: vmcnt in bits 3:0 and
-      // 15:14, expcnt 6:4, lgkmcnt 11:8)
-      const int after = ntiles - 1 - tile;
-      if (after >= 2) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoads));
-      } else if (after == 1) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      }
-      __builtin_amdgcn_s_barrier();
-      // the buffer of tile + kAhead was last read in tile - 1, which every
-      // wave has finished at the barrier above
-      if (tile + kAhead < ntiles) issue(tile + kAhead, (tile + kAhead) % kBufs);
-      const uint8_t* tb = smem + buf * kBufBytes;
-      const int nvalid = (int)(s1 - (s0 + (int64_t)tile * kTile));   // > kTile except at the end
-
-      // ---- logits for both 16-token halves and both head blocks; K operands
-      // are read two chunks ahead of the MFMAs that use them
-      f32x4_t s[2][2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) s[u][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      auto kread = [&](int c, int u) {
-        const uint8_t* p = c < 16 ? tb + k_main + (16 * u * kMainStride + 4 * c) * 16
-                                  : tb + k_tail + (16 * u * kTailStride + 4 * (c - 16)) * 16;
-        return *reinterpret_cast<const uint4*>(p);
-      };
-      uint4 ka0 = kread(0, 0), ka1 = kread(0, 1);
-      uint4 kb0 = kread(1, 0), kb1 = kread(1, 1);
-#pragma unroll
-      for (int c = 0; c < 18; ++c) {
-        const uint4 k0 = ka0, k1 = ka1;
-        ka0 = kb0;
-        ka1 = kb1;
-        if (c + 2 < 18) {
-          kb0 = kread(c + 2, 0);
-          kb1 = kread(c + 2, 1);
-        }
-        const bf16x8_t a0 = as_bf16x8(k0.x, k0.y, k0.z, k0.w);
-        const bf16x8_t a1 = as_bf16x8(k1.x, k1.y, k1.z, k1.w);
-        s[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qop[0][c], s[0][0], 0, 0, 0);
-        s[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qop[0][c], s[1][0], 0, 0, 0);
-        s[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qop[1][c], s[0][1], 0, 0, 0);
-        s[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qop[1][c], s[1][1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      // ---- softmax weights per head; lane (n, g) holds the logits of head n
-      // for tokens tok[0..7]
-      bf16x8_t pop[2], pol[2];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        float x[8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[4 * u + i] = s[u][hb][i];
-        if (nvalid < kTile) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = tok[e] < nvalid ? x[e] : -INFINITY;
-        }
-        float tmax = x[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-        const float tmax2 = rows4_max(tmax) * c2;
-        if (max_only) {
-          m2[hb] = fmaxf(m2[hb], tmax2);
-          continue;
-        }
-        if (m2[hb] == -INFINITY) m2[hb] = tmax2;      // first tile: acc is still zero
-        overflow |= (tmax2 > m2[hb] + kHeadroom);
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(x[e], c2, -m2[hb]));  // masked logits give exp2(-inf) = 0
-          lsum[hb] += p[e];
-        }
-        uint32_t ph[4], pl[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t b0 = __float_as_uint(p[2 * i]), b1 = __float_as_uint(p[2 * i + 1]);
-          ph[i] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-          pl[i] = pack_bf16(p[2 * i] - __uint_as_float(b0 & 0xFFFF0000u),
-                            p[2 * i + 1] - __uint_as_float(b1 & 0xFFFF0000u));
-        }
-        pop[hb] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
-        pol[hb] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
-      }
-      if (max_only) continue;
-
-      // ---- O^T += V^T P^T over 32 blocks of 16 value columns; V^T operands
-      // are read two blocks ahead of their MFMAs
-      const uint8_t* vl0 = tb + v_off;                        // tokens of half 0
-      const uint8_t* vl1 = vl0 + 16 * kMainStride * 16;       // tokens of half 1
-      auto vread = [&](const uint8_t* p, int blk) {
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 2 * blk * 16));
-      };
-      s16x4_t va0 = vread(vl0, 0), va1 = vread(vl1, 0);
-      s16x4_t vb0 = vread(vl0, 1), vb1 = vread(vl1, 1);
-#pragma unroll
-      for (int blk = 0; blk < 32; ++blk) {
-        const s16x4_t v0 = va0, v1 = va1;
-        va0 = vb0;
-        va1 = vb1;
-        if (blk + 2 < 32) {
-          vb0 = vread(vl0, blk + 2);
-          vb1 = vread(vl1, blk + 2);
-        }
-        const uint2 w0 = __builtin_bit_cast(uint2, v0);
-        const uint2 w1 = __builtin_bit_cast(uint2, v1);
-        const bf16x8_t vop = as_bf16x8(w0.x, w0.y, w1.x, w1.y);
-        acc[0][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[0], acc[0][blk], 0, 0, 0);
-        acc[1][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[1], acc[1][blk], 0, 0, 0);
-        acc[0][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pol[0], acc[0][blk], 0, 0, 0);
-        acc[1][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pol[1], acc[1][blk], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // every wave is past its last LDS read before the buffers are refilled
-    const int any_overflow = __syncthreads_or(overflow);
     if (max_only) {
+      // logits-only pass: each head's exact max over the shard
+      for (int tile = 0; tile < ntiles; ++tile) {
+        const int nvalid = tile_ready(tile);
+        f32x16_t sl;
+        tile_logits(smem + (tile % kBufs) * kBufBytes, sl);
+        m2 = fmaxf(m2, tile_max2(sl, nvalid));
+      }
+      __syncthreads();           // every wave is past its last LDS read
       max_only = false;          // m2 now holds each head's exact max
       continue;
     }
-    if (!any_overflow) break;
-    max_only = true;
-    m2[0] = m2[1] = -INFINITY;
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int buf = tile % kBufs;
+      const int nvalid = tile_ready(tile);
+      const uint8_t* tb = smem + buf * kBufBytes;
+      f32x16_t sl;
+      tile_logits(tb, sl);
+
+      // ---- softmax weights of head l32: this lane's 16 tokens
+      // 8 (e / 4) + 4 h2 + e % 4, the other 16 in lane l ^ 32
+      float x[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = sl[e];
+      if (nvalid < kTile) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = 8 * (e >> 2) + 4 * h2 + (e & 3) < nvalid ? x[e] : -INFINITY;
+      }
+      const float tmax2 = tile_max2(sl, nvalid);
+      if (m2 == -INFINITY) m2 = tmax2;      // first tile: acc is still zero
+      overflow |= (tmax2 > m2 + kHeadroom);
+      // P = 2^(x c2 - m + kPOffset) (masked logits give exp2(-inf) = 0),
+      // packed to fp16 toward zero; lsum takes the exact weights, lsum16 the
+      // fp16 ones the PV product uses
+      uint32_t ph[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = fast_exp2(fmaf(x[2 * i], c2, kPOffset - m2));
+        const float p1 = fast_exp2(fmaf(x[2 * i + 1], c2, kPOffset - m2));
+        lsum += p0 + p1;
+        const h16x2_t pp = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+        lsum16 = __builtin_amdgcn_fdot2(pp, h16x2_t{(__fp16)1.0f, (__fp16)1.0f}, lsum16, false);
+        ph[i] = __builtin_bit_cast(uint32_t, pp);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        *(lds_u32x4*)(uintptr_t)(p_lds + (uint32_t)(((2 * wave + st) * 64 + lane) * 16)) =
+            u32x4_t{ph[4 * st], ph[4 * st + 1], ph[4 * st + 2], ph[4 * st + 3]};
+      // every wave's weights are in LDS
+      __syncthreads();
+
+      // ---- O^T += V^T P^T: this wave's 4 blocks of 32 value columns against
+      // the weights of all 4 head blocks, two 16-token steps each; V^T
+      // operands converted to fp16 one step ahead of their MFMAs
+      if (vscaled) {
+        // rerun with this wave's V scaled by vsc (a V element beyond fp16):
+        // scale its 128 columns of the tile in LDS, which only this wave
+        // reads from here on (every logits read of the tile is done), exactly
+        // (a power of two; bf16 keeps fp32's exponent range)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = 64 * i + lane;          // 16-byte chunk: row c / 16, column chunk c % 16
+          lds_u32x4* q16 = (lds_u32x4*)(uintptr_t)(lds0 + (uint32_t)(buf * kBufBytes) +
+                                                   (uint32_t)((c / 16) * kMainStride * 16 + 256 * wave + (c % 16) * 16));
+          u32x4_t w = *q16;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float lo = __uint_as_float(w[k] << 16) * vsc, hi = __uint_as_float(w[k] & 0xFFFF0000u) * vsc;
+            w[k] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+          }
+          *q16 = w;
+        }
+      }
+      const uint8_t* vbase = tb + v_off + 2 * 128 * wave;
+      auto vraw = [&](int d, int st) {
+        const uint8_t* p = vbase + 2 * 32 * d + 16 * st * kMainStride * 16;
+        const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+        const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                      (lds_s16x4_t*)(p + 8 * kMainStride * 16)));
+        return u32x4_t{w0.x, w0.y, w1.x, w1.y};
+      };
+      u32x4_t pw[4][2];
+#pragma unroll
+      for (int H = 0; H < 4; ++H)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          pw[H][st] = *(const lds_u32x4*)(uintptr_t)(p_lds + (uint32_t)(((2 * H + st) * 64 + lane) * 16));
+      u32x4_t vn = vraw(0, 0);
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) {
+        const int d = ds >> 1, st = ds & 1;
+        const u32x4_t vr = vn;
+        if (ds + 1 < 8) vn = vraw((ds + 1) >> 1, (ds + 1) & 1);
+        u32x4_t vh;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = __uint_as_float(vr[k] << 16), hi = __uint_as_float(vr[k] & 0xFFFF0000u);
+          vmax = fmaxf(fmaxf(vmax, fabsf(lo)), fabsf(hi));
+          vh[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        }
+        const f16x8_t va = __builtin_bit_cast(f16x8_t, vh);
+#pragma unroll
+        for (int H = 0; H < 4; ++H)
+          acc[d][H] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, __builtin_bit_cast(f16x8_t, pw[H][st]), acc[d][H], 0, 0, 0);
+      }
+    }
+    // a V element of this wave's columns beyond fp16 (on the unscaled pass)
+    if (!vscaled && __any(vmax >= 65520.0f)) overflow |= 2;
+    // every wave is past its last LDS read before the buffers are refilled
+    // (bit 0: a logit beyond the headroom; bit 1: a V element beyond fp16)
+    const int flags = __syncthreads_or(overflow);
+    if (!flags) break;
+    if (overflow & 2) {
+      // V x 2^-k, with the wave's largest |V| below 2^(14 + k), fits fp16
+      // (an infinite V element stays infinite: k = 0)
+      const float wmax = rows4_max(row16_max(vmax));
+      const int k = __builtin_amdgcn_readfirstlane(isinf(wmax) ? 0 : min(120, (int)ceilf(fast_log2(wmax)) - 14));
+      vsc = __uint_as_float((uint32_t)(127 - k) << 23);
+      vscaled = k > 0;
+    }
+    if (flags & 1) {
+      max_only = true;
+      m2 = -INFINITY;
+    }                            // else: the same reference max again
   }
 
-  // ---- write the normalized partial of this wave's 32 heads
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const float lt = rows4_sum(lsum[hb]);
-    const bool empty = (m2[hb] == -INFINITY);
-    const float inv = empty ? 0.0f : 1.0f / lt;
-    const int h = head0 + 16 * hb + r16;
-    float* orow = a.o_part + (orow0 + h) * kDv;
-#pragma unroll
-    for (int blk = 0; blk < 32; ++blk) {
-      const f32x4_t v = acc[hb][blk] * inv;
-      *reinterpret_cast<float4*>(orow + 16 * blk + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+  // ---- lse of this wave's 32 heads; the fp16 weight sums of all 128 heads
+  // through LDS (the buffers are idle after the final barrier above)
+  {
+    const float lt = half_sum(lsum);
+    const float l16 = half_sum(lsum16);
+    const bool empty = (m2 == -INFINITY);
+    const int h = wave * 32 + l32;
+    if (h2 == 0) {
+      a.lse_part[orow0 + kvh * kHeads + h] = empty ? -INFINITY : (m2 - kPOffset + fast_log2(lt)) * kLn2;
+      sum_lds[h] = empty ? 0.0f : l16;
     }
-    if (g == 0)
-      a.lse_part[orow0 + h] = empty ? -INFINITY : (m2[hb] + fast_log2(lt)) * kLn2;
+  }
+  __syncthreads();
+  // ---- write this wave's 128 value columns of every head, normalized:
+  // element e of acc[d][H] is column 128 wave + 32 d + 8 (e / 4) + 4 h2 + e % 4
+#pragma unroll
+  for (int H = 0; H < 4; ++H) {
+    const int h = 32 * H + l32;
+    const float l16 = sum_lds[h];
+    const float inv = l16 > 0.0f ? 1.0f / (l16 * vsc) : 0.0f;
+    float* orow = a.o_part + (orow0 + kvh * kHeads + h) * kDv + 128 * wave + 4 * h2;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(orow + 32 * d + 8 * j) =
+            make_float4(acc[d][H][4 * j] * inv, acc[d][H][4 * j + 1] * inv, acc[d][H][4 * j + 2] * inv,
+                        acc[d][H][4 * j + 3] * inv);
   }
 }
 
-constexpr size_t kSmemBytes = (size_t)kBufs * kBufBytes;
+constexpr size_t kSmemBytes = (size_t)kBufs * kBufBytes + kPBytes;
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 static_assert((kTile - 1) * kMainStride * 16 + kMainRowBytes <= kMainBytes, "row loads stay in the main region");
 static_assert(kMainBytes + (kTile - 4) * kTailStride * 16 + 4 * kTailStride * 16 <= kBufBytes,

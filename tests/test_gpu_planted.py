@@ -10,6 +10,7 @@
 * MXFP4 block exponents far from 127 in K and in V, and all-zero blocks at
   the extreme exponents.
 * fp8 scales that are negative or zero.
+* Latent-cache values beyond fp16's range.
 
 Every case compares every shard partial and the merged output with the
 float64 oracle at the format's tolerances (the exactness of the split is the
@@ -144,6 +145,46 @@ def test_rising_logits_latent(T):
     w = _wl("bf16", T, B=1, Hq=128, Hkv=1, D=576, Dv=512, S=704, alias=True)
     inp, q = _ramp(w, 0.3)
     _check_inputs(w, inp, q, "paged", 3, [(700,)])
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_latent_values_beyond_fp16(layout):
+    """The latent kernel takes V into its PV product as fp16; V elements of
+    magnitude 2^18 .. 2^19 (beyond fp16's range) in the column slices of
+    three of its four waves make it rerun the shard with those waves' V
+    scaled by a power of two.  The queries are zero on the planted dims, so
+    the logits are those of the generated cache; the planted columns are
+    compared after division by 2^19, the others as they are."""
+    import numpy as np
+    w = _wl("bf16", 1, B=2, Hq=128, Hkv=1, D=576, Dv=512, S=704, alias=True, seed=81)
+    inp = kvgen.make_inputs(w)
+    q = np.ascontiguousarray(inp.q.reshape(w.B, 1, w.Hq, w.Dqk)).copy()
+    big = np.array([5, 300, 511])
+    q[..., big] = 0
+    rng = np.random.default_rng(4)
+    for b in range(w.B):
+        rows = rng.choice(w.S_max, size=40, replace=False)
+        vals = rng.choice([-1.0, 1.0], size=(40, 3)) * rng.uniform(2.0 ** 18, 2.0 ** 19, size=(40, 3))
+        inp.k_data[b, 0][np.ix_(rows, big)] = _bf16_bits(vals)
+    normal = np.setdiff1d(np.arange(w.Dv), big)
+    T, S = 1, w.S_max
+    if layout == "paged":
+        cache, nb = _paged_from_contiguous(w, inp, 16, S // 16, np.random.default_rng(3))
+        cache["num_blocks"] = nb
+    else:
+        cache = {"k": inp.k_data, "k_scale": inp.k_scale, "v": inp.v_data, "v_scale": inp.v_scale}
+    p = oracle.Problem(w.B, w.Hq, w.Hkv, w.Dqk, w.Dv, S, w.q_dtype, w.kv_dtype, w.v_aliases_k)
+    for kvp, seq in ((1, (704, 333)), (3, (700, 64))):
+        seq = np.asarray(seq, dtype=np.int32)
+        what = "%s latent big-V kvp=%d L=%s" % (layout, kvp, tuple(int(x) for x in seq))
+        gc.log("  case " + what)
+        o_part, lse_part, o, lse = _run(w, T, layout, kvp, S, q, cache, seq)
+        ref_po, ref_pl = op.decode_partials_tokens(p, T, layout, kvp, q, cache, seq)
+        ref_o, ref_l = op.decode_tokens(p, T, layout, kvp, q, cache, seq)
+        for got, gl, ref, rl, tag in ((o_part, lse_part, ref_po, ref_pl, "partials"), (o, lse, ref_o, ref_l, "merged")):
+            gc.compare(got[..., normal], gl, ref[..., normal], rl, "bf16", what + " " + tag + " other columns")
+            gc.compare(got[..., big] / 2.0 ** 19, gl, ref[..., big] / 2.0 ** 19, rl, "bf16",
+                       what + " " + tag + " planted columns / 2^19")
 
 
 @pytest.mark.parametrize("kv", ["f32", "fp8"])
