@@ -38,21 +38,21 @@ METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S
 # counters were taken on).  Changed kernel code no longer matches, and the
 # bench then reports traffic as null.  Summaries are under profiles/.
 TRAFFIC = {
-    ("helix_fp8", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 17328989465,
-    ("helix_fp8", "paged16", 32, 1, "f0510cf1dd96ce3c"): 17350776854,
-    ("helix_fp8", "contiguous", 32, 4, "f0510cf1dd96ce3c"): 18638267018,
-    ("helix_mxfp4", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 9230341008,
-    ("gqa_bf16_varlen", "contiguous", 16, 1, "f0510cf1dd96ce3c"): 3482922455,
-    ("gqa_bf16_varlen", "contiguous", 16, 4, "f0510cf1dd96ce3c"): 3487459233,
-    ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 4901559411,
+    ("helix_fp8", "contiguous", 32, 1, "aab509e483b02edb"): 17210927688,
+    ("helix_fp8", "contiguous", 128, 1, "aab509e483b02edb"): 17281429084,
+    ("helix_fp8", "contiguous", 32, 4, "aab509e483b02edb"): 17252396058,
+    ("helix_mxfp4", "contiguous", 32, 1, "aab509e483b02edb"): 9162409197,
+    ("helix_mxfp4", "contiguous", 128, 1, "aab509e483b02edb"): 9235992371,
+    ("gqa_bf16_varlen", "contiguous", 16, 1, "aab509e483b02edb"): 3495859141,
+    ("mla_bf16", "contiguous", 32, 1, "5cb792b77c5399b4"): 4901142751,
 }
 # Fraction of the partial kernel's SIMD cycles with the matrix cores busy,
 # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs), from a
 # rocprofv3 --pmc run; same keys as TRAFFIC.
 MFMA_BUSY = {
-    ("mla_bf16", "contiguous", 32, 1, "491f6187eb3d244f"): 0.5503,
-    ("helix_mxfp4", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 0.3513,
-    ("helix_fp8", "contiguous", 32, 1, "f0510cf1dd96ce3c"): 0.1730,
+    ("mla_bf16", "contiguous", 32, 1, "5cb792b77c5399b4"): 0.4013,
+    ("helix_mxfp4", "contiguous", 32, 1, "aab509e483b02edb"): 0.2187,
+    ("helix_fp8", "contiguous", 32, 1, "aab509e483b02edb"): 0.1302,
 }
 _GQA_SOURCES = ("partial_gqa_mfma.hip", "gqa_mfma_kernel.hpp", "partial_gqa_mfma_tokens.hip")
 KERNEL_SOURCES = {"bf16": _GQA_SOURCES, "fp8": _GQA_SOURCES, "mxfp4": _GQA_SOURCES,

@@ -1,7 +1,7 @@
 // Split-KV partial attention for a GQA group of up to 16 query heads on MFMA:
 // the kernel template, shared by the translation units that instantiate it
-// (partial_gqa_mfma.hip: accumulators in VGPRs; partial_gqa_mfma_t4.hip:
-// the four-token one-wave instances, accumulators in AGPRs).
+// (partial_gqa_mfma.hip: accumulators in VGPRs; partial_gqa_mfma_tokens.hip:
+// the one-wave two-token instances, accumulators in AGPRs).
 //
 // With 16 query heads sharing one KV head, every cached K and V element feeds
 // 16 multiply-adds, which is more arithmetic per HBM byte than the fp32 vector
@@ -38,10 +38,11 @@
 // Work split: one workgroup of 4 waves per (shard j, request b, KV head,
 // chunk of query tokens: one token for a single-token decode, two or four for
 // a multi-token turn); wave w takes the shard's 32-token tiles w, w+4, w+8, ...
-// and, for one token, keeps the loads of its next one (bf16) or two (fp8,
-// MXFP4: smaller tiles) tiles in flight while computing the current one, so
-// enough bytes are outstanding to cover HBM latency at 2-3 waves per SIMD.
-// Several tokens share every loaded tile (see TW below).
+// and, for one token, keeps the loads of its next one (bf16) or three (fp8,
+// MXFP4: smaller tiles) tiles in flight while computing the current one (fp8
+// at one wave per SIMD, MXFP4 at two).  With enough shard units the one-wave
+// split (SOLO below) replaces the four-wave one.  Several tokens share every
+// loaded tile (see TW below).
 // Lane (r, g) = (lane % 16, lane / 16):
 //  * K: lane (r, g) loads token r of each 16-token half-tile, bytes
 //    [64i + 16g, 64i + 16g + 16) of the row for each 16-byte load i, so each
@@ -56,7 +57,8 @@
 //    (running max, partial sum) is per lane and needs no transposes; the O^T
 //    accumulator of lane (n, g) is head n, dv in [32g, 32g + 32).
 // The running max is only moved when a tile's max exceeds it by more than 2^8
-// (in the exp2 domain); the stale max is exact algebra and keeps P <= 256.
+// (in the exp2 domain); the stale max is exact algebra and keeps P <= 2^8
+// (fp16 weights, offset by 2^7: <= 2^15).
 // At the end the four waves' (max, sums, acc) states are merged through LDS
 // and the normalized partial o and its natural-log lse are written.
 #pragma once
