@@ -54,7 +54,8 @@ MFMA_BUSY = {
     ("helix_mxfp4", "contiguous", 32, 1, "aab509e483b02edb"): 0.2187,
     ("helix_fp8", "contiguous", 32, 1, "aab509e483b02edb"): 0.1302,
 }
-_GQA_SOURCES = ("partial_gqa_mfma.hip", "gqa_mfma_kernel.hpp", "partial_gqa_mfma_tokens.hip")
+_GQA_SOURCES = ("partial_gqa_mfma.hip", "gqa_mfma_kernel.hpp", "partial_gqa_mfma_tokens.hip",
+                "partial_gqa_tokens32.hip")
 KERNEL_SOURCES = {"bf16": _GQA_SOURCES, "fp8": _GQA_SOURCES, "mxfp4": _GQA_SOURCES,
                   "f32": ("partial_valu.hip",), "latent": ("partial_mla_mfma.hip",)}
 
@@ -146,6 +147,10 @@ ARITH = {
            "log2 multiplier); V decoded exactly to fp16, P.V on fp16 MFMA with P = 2^(s - m + 7) rounded to "
            "fp16 and normalized by the sum of those fp16 weights (one more MFMA); fp32 accumulation, softmax "
            "and log-sum-exp",
+    "fp8_tokens": "bf16 MFMA logits (32x32x16, the columns are (query token, head) pairs) on K decoded exactly "
+                  "from E4M3 once for all tokens; V decoded exactly to fp16, P.V on fp16 MFMA (32x32x16) with "
+                  "P = 2^(s - m + 7) rounded to fp16 and normalized by the sum of those fp16 weights; fp32 "
+                  "accumulation, softmax and log-sum-exp",
     "mxfp4": "bf16 MFMA logits (16x16x32) on K decoded exactly from E2M1 with its E8M0 block exponents; V "
              "decoded exactly to fp16 with its block scales, P.V on fp16 MFMA with P = 2^(s - m + 7) rounded to "
              "fp16 and normalized by the sum of those fp16 weights (tiles whose V exponents leave fp16's range: "
@@ -155,7 +160,8 @@ ARITH = {
               "normalized by the sum of those fp16 weights; tiles staged through an LDS ring, the weights "
               "exchanged between the 4 waves through LDS; fp32 accumulation, softmax and log-sum-exp",
 }
-DTYPE = {"f32": "f32", "bf16": "bf16", "fp8": "bf16+fp16", "mxfp4": "bf16+fp16", "latent": "bf16+fp16"}
+DTYPE = {"f32": "f32", "bf16": "bf16", "fp8": "bf16+fp16", "fp8_tokens": "bf16+fp16", "mxfp4": "bf16+fp16",
+         "latent": "bf16+fp16"}
 # Executed P.V flops per algorithmic ones on the latent kernel (one fp16
 # product).
 LATENT_PV_PASSES = 1
@@ -268,6 +274,8 @@ def measure(args, name, kvp_req, T, layout, block_len, timing_extras=True):
     lay_key = layout + (str(block_len) if layout == "paged" else "")
     traffic = TRAFFIC.get((w.name, lay_key, kvp, T, khash))
     fam = "latent" if w.v_aliases_k else w.kv_dtype
+    if fam == "fp8" and T in (3, 4) and w.Hq == 16 * w.Hkv and kvp * w.B * w.Hkv >= 1024:
+        fam = "fp8_tokens"   # the one-wave kernel with the tokens as matrix-core columns
     res = {
         "value": round(value, 2),
         "unit": "GB/s",

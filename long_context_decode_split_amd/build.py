@@ -21,15 +21,17 @@ LIB = os.path.join(PKG, "libkvd.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "lse_merge.hip", "partial_valu.hip", "partial_gqa_mfma.hip",
-           "partial_gqa_mfma_tokens.hip", "partial_mla_mfma.hip", "append_kv.hip"]
+           "partial_gqa_mfma_tokens.hip", "partial_gqa_tokens32.hip", "partial_mla_mfma.hip", "append_kv.hip"]
 
-# Per-source extra flags.  The GQA kernel keeps its MFMA accumulators in
-# ordinary VGPRs (it has room, and the occasional vector-ALU rescale of the
-# accumulator would otherwise make the compiler shuttle them between AGPRs
-# and VGPRs every tile); its multi-token one-wave instances
+# Per-source extra flags.  The GQA kernels keep their MFMA accumulators in
+# ordinary VGPRs (they have room, and the occasional vector-ALU rescale of
+# the accumulator would otherwise make the compiler shuttle them between
+# AGPRs and VGPRs every tile; the four-token kernel holds its query operands
+# in AGPRs instead); the two-token one-wave instances
 # (partial_gqa_mfma_tokens.hip) and the latent kernel need the AGPRs for their
 # accumulators and keep the default.
-SOURCE_FLAGS = {"partial_gqa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"partial_gqa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "partial_gqa_tokens32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

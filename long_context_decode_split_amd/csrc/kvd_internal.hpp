@@ -71,6 +71,12 @@ hipError_t launch_partial_gqa_mfma(const PartialArgs& a, hipStream_t stream);
 // cache, one (shard, two-token chunk) per wave (partial_gqa_mfma_tokens.hip).
 hipError_t launch_gqa_solo_tokens(const PartialArgs& a, hipStream_t stream);
 
+// Three or four query tokens of an fp8 cache with 16 query heads per KV head:
+// one wave per shard unit, the tokens as columns of 32x32 MFMAs
+// (partial_gqa_tokens32.hip).
+bool gqa_tokens32_supports(const PartialArgs& a);
+hipError_t launch_gqa_tokens32(const PartialArgs& a, hipStream_t stream);
+
 bool mla_mfma_supports(const PartialArgs& a);
 hipError_t launch_partial_mla_mfma(const PartialArgs& a, hipStream_t stream);
 

@@ -80,7 +80,10 @@ hipError_t launch_gqa3(const PartialArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)blocks), block(kThreads);
   const int64_t units = (int64_t)a.kvp * a.B * a.Hkv;
   const int nsh = tw == 1 ? solo_shards<KV>(units) : 0;
-  if (KV != kBF16 && a.T >= 2 && a.T <= 4 && units >= Layout<KV>::kSoloTokenUnits) {
+  if (KV == kFP8 && a.T >= 3 && a.T <= 4 && units >= Layout<KV>::kSoloTokenUnits && gqa_tokens32_supports(a)) {
+    // one wave per shard unit, all tokens on 32x32 MFMAs
+    return launch_gqa_tokens32(a, stream);
+  } else if (KV != kBF16 && a.T >= 2 && a.T <= 4 && units >= Layout<KV>::kSoloTokenUnits) {
     // one wave per (shard, two-token chunk)
     return launch_gqa_solo_tokens(a, stream);
   } else if (nsh > 0) {

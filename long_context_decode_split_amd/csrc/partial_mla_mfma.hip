@@ -105,7 +105,11 @@ __device__ __forceinline__ void logit_mfma(f32x16_t& acc, const uint4& k, const 
   else
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kv), "v"(qv));
 }
-__device__ __forceinline__ void logit_mfma_drain() { asm volatile("s_nop 15" ::: "memory"); }
+// The drain names both accumulators as operands, so no read of them can be
+// scheduled between the last MFMA and the padding.
+__device__ __forceinline__ void logit_mfma_drain(f32x16_t& a0, f32x16_t& a1) {
+  asm volatile("s_nop 15" : "+v"(a0), "+v"(a1));
+}
 
 // PAGED: rows are found through the block table (paged cache layout).
 template <bool PAGED>
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
       else
         logit_mfma(sl, k0, qop[c], i == 0);
     }
-    logit_mfma_drain();
+    logit_mfma_drain(sl, sl2);
 #pragma unroll
     for (int e = 0; e < 16; ++e) sl[e] += sl2[e];
   };

@@ -14,7 +14,7 @@ def test_kernel_sources_exist():
 
 
 def test_every_family_is_described():
-    for fam in ("f32", "bf16", "fp8", "mxfp4", "latent"):
+    for fam in ("f32", "bf16", "fp8", "fp8_tokens", "mxfp4", "latent"):
         assert bench.ARITH[fam] and bench.DTYPE[fam]
 
 

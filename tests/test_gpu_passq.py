@@ -101,6 +101,23 @@ def test_multi_token_partials_and_merge(layout, kv, shape):
     _check(w, T, layout, kvp, S, seqs, seed=7)
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("T", [3, 4])
+def test_token_cut_at_shard_start(layout, T):
+    """fp8, 16 query heads per KV head, 1024 shard units (the one-wave kernel
+    that puts the query tokens in the matrix-core columns): lengths that put a
+    shard boundary at a later token's cut, so that within one tile some token
+    columns see no row while the others see one to three (their running max
+    moves while the others' stays at -inf), and a request of T - 1 rows,
+    whose first token sees nothing at all."""
+    kvp, S = 64, 1024
+    w = _wl("fp8", B=2, S=S, Hq=128, Hkv=8, D=128)
+    # 16-row shards (the rounded-up share of at most 1024 rows): shard 40
+    # starts at row 640
+    seqs = [(640 + T - 1, T - 1), (640 + T - 2, 656)]
+    _check(w, T, layout, kvp, S, seqs, seed=12)
+
+
 @pytest.mark.parametrize("T", [1, 2, 16, 40])
 def test_token_counts_gqa_fp8(T):
     """The matrix-core GQA kernel over token counts that leave the last group
