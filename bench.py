@@ -38,35 +38,39 @@ METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S
 # counters were taken on).  Changed kernel code no longer matches, and the
 # bench then reports traffic as null.  Summaries are under profiles/.
 TRAFFIC = {
-    ("helix_fp8", "contiguous", 32, 1, "aab509e483b02edb"): 17210927688,
-    ("helix_fp8", "contiguous", 128, 1, "aab509e483b02edb"): 17281429084,
-    ("helix_fp8", "contiguous", 32, 4, "aab509e483b02edb"): 17252396058,
-    ("helix_mxfp4", "contiguous", 32, 1, "aab509e483b02edb"): 9162409197,
-    ("helix_mxfp4", "contiguous", 128, 1, "aab509e483b02edb"): 9235992371,
-    ("gqa_bf16_varlen", "contiguous", 16, 1, "aab509e483b02edb"): 3495859141,
-    ("mla_bf16", "contiguous", 32, 1, "5cb792b77c5399b4"): 4901142751,
+    ("helix_fp8", "contiguous", 32, 1, "bf13adca9bbd9ae0"): 17211269834,
+    ("helix_fp8", "contiguous", 128, 1, "bf13adca9bbd9ae0"): 17281780756,
+    ("helix_fp8", "contiguous", 32, 4, "72c39fc00755a1a4"): 17249117166,
+    ("helix_fp8", "contiguous", 32, 3, "72c39fc00755a1a4"): 17231770591,
+    ("helix_fp8", "contiguous", 128, 4, "72c39fc00755a1a4"): 17458637806,
+    ("helix_mxfp4", "contiguous", 32, 1, "bf13adca9bbd9ae0"): 9162223241,
+    ("helix_mxfp4", "contiguous", 128, 1, "bf13adca9bbd9ae0"): 9236260755,
+    ("gqa_bf16_varlen", "contiguous", 16, 1, "bf13adca9bbd9ae0"): 3496245251,
+    ("mla_bf16", "contiguous", 32, 1, "778a9c2893ba45b9"): 4901145396,
 }
 # Fraction of the partial kernel's SIMD cycles with the matrix cores busy,
 # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs), from a
 # rocprofv3 --pmc run; same keys as TRAFFIC.
 MFMA_BUSY = {
-    ("mla_bf16", "contiguous", 32, 1, "5cb792b77c5399b4"): 0.4013,
-    ("helix_mxfp4", "contiguous", 32, 1, "aab509e483b02edb"): 0.2187,
-    ("helix_fp8", "contiguous", 32, 1, "aab509e483b02edb"): 0.1302,
+    ("mla_bf16", "contiguous", 32, 1, "778a9c2893ba45b9"): 0.3919,
+    ("helix_mxfp4", "contiguous", 32, 1, "bf13adca9bbd9ae0"): 0.2201,
+    ("helix_fp8", "contiguous", 32, 1, "bf13adca9bbd9ae0"): 0.1284,
+    ("helix_fp8", "contiguous", 32, 4, "72c39fc00755a1a4"): 0.3598,
 }
-_GQA_SOURCES = ("partial_gqa_mfma.hip", "gqa_mfma_kernel.hpp", "partial_gqa_mfma_tokens.hip",
-                "partial_gqa_tokens32.hip")
+_GQA_SOURCES = ("partial_gqa_mfma.hip", "gqa_mfma_kernel.hpp", "partial_gqa_mfma_tokens.hip")
 KERNEL_SOURCES = {"bf16": _GQA_SOURCES, "fp8": _GQA_SOURCES, "mxfp4": _GQA_SOURCES,
+                  "fp8_tokens": ("partial_gqa_tokens32.hip", "partial_gqa_mfma.hip"),
                   "f32": ("partial_valu.hip",), "latent": ("partial_mla_mfma.hip",)}
 
 
-def kernel_hash(kv_dtype, mla=False):
-    """sha256 prefix of the partial kernel's code (its source files plus the
-    shared device header), with // comments and blank space removed, so that
-    comment edits keep the recorded counters."""
+def kernel_hash(fam):
+    """sha256 prefix of the code of kernel family `fam` (a KERNEL_SOURCES key:
+    its source files, the launcher that routes to it, and the shared device
+    header), with // comments and blank space removed, so that comment edits
+    keep the recorded counters."""
     import hashlib
     import re
-    names = KERNEL_SOURCES["latent" if mla else kv_dtype]
+    names = KERNEL_SOURCES[fam]
     h = hashlib.sha256()
     for f in names + ("kvd_device.hpp",):
         with open(os.path.join(HERE, "long_context_decode_split_amd", "csrc", f)) as fh:
@@ -270,12 +274,12 @@ def measure(args, name, kvp_req, T, layout, block_len, timing_extras=True):
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (partial_avg * 1e-3) / 1e9
     peak = roofline.HBM_BYTES_PER_S / 1e9
-    khash = kernel_hash(w.kv_dtype, mla=w.v_aliases_k)
-    lay_key = layout + (str(block_len) if layout == "paged" else "")
-    traffic = TRAFFIC.get((w.name, lay_key, kvp, T, khash))
     fam = "latent" if w.v_aliases_k else w.kv_dtype
     if fam == "fp8" and T in (3, 4) and w.Hq == 16 * w.Hkv and kvp * w.B * w.Hkv >= 1024:
         fam = "fp8_tokens"   # the one-wave kernel with the tokens as matrix-core columns
+    khash = kernel_hash(fam)
+    lay_key = layout + (str(block_len) if layout == "paged" else "")
+    traffic = TRAFFIC.get((w.name, lay_key, kvp, T, khash))
     res = {
         "value": round(value, 2),
         "unit": "GB/s",
