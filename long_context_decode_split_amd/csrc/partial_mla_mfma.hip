@@ -23,8 +23,14 @@
 // value columns 128w .. 128w+127 of all 128 heads (256 AGPRs).  Per tile a
 // wave reads the whole K tile for its logits and only its quarter of V.
 //
+// The tile loop is software-pipelined: the softmax of tile t - 1 runs in
+// small pieces between the logits MFMAs of tile t (the vector ALU proceeds
+// under a 32x32 MFMA), and once every wave's weights of tile t - 1 are in LDS
+// the PV product of tile t - 1 follows, its V operands converted between its
+// MFMAs one step ahead.
+//
 // Tiles travel HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a
-// ring of kBufs buffers, kAhead = 3 tiles ahead.  A buffer has two regions: the first
+// ring of kBufs buffers, kAhead = 2 tiles ahead.  A buffer has two regions: the first
 // 1024 bytes of each of the 32 rows (dims 0..511) at a stride of 65 16-byte
 // slots, one row per load instruction, and the last 128 bytes (dims 512..575)
 // at a stride of 9 slots, four rows per load instruction.  Every source
@@ -65,9 +71,10 @@ constexpr int kMainBytes = kTile * kMainStride * 16;   // 33280
 constexpr int kTailBytes = kTile * kTailStride * 16;   // 4608
 constexpr int kBufBytes = kMainBytes + kTailBytes;     // 37888
 constexpr int kBufs = 4;
-constexpr int kAhead = kBufs - 1;           // tiles in flight ahead of the one computed
+constexpr int kAhead = 2;                  // tiles issued ahead of the one whose logits run
 constexpr int kLoads = kRowsPerWave + kRowsPerWave / 4;  // load instructions per wave per tile
-constexpr int kKAhead = 2;                 // K operand reads in flight ahead of the logits MFMAs
+constexpr int kSoftPieces = 18;            // softmax pieces per tile (two maxima, 16 weights)
+constexpr int kKAhead = 4;                 // K operand reads in flight ahead of the logits MFMAs
 constexpr int kPBytes = 8 * 64 * 16;        // fp16 weights of one tile, all 128 heads
 // The fp16 weights are 2^kPOffset times exp2(logit - reference max): at most
 // 2^(kPOffset + kHeadroom) = 2^15 < 65504 while no logit exceeds the
@@ -109,6 +116,15 @@ __device__ __forceinline__ void logit_mfma(f32x16_t& acc, const uint4& k, const 
 // scheduled between the last MFMA and the padding.
 __device__ __forceinline__ void logit_mfma_drain(f32x16_t& a0, f32x16_t& a1) {
   asm volatile("s_nop 15" : "+v"(a0), "+v"(a1));
+}
+
+// A wave-uniform pointer as scalar registers (the direct-to-LDS load takes
+// its base address there).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
 // PAGED: rows are found through the block table (paged cache layout).
@@ -171,21 +187,28 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   // Rotary-dim loads: lane i < 36 fills slot i of a 4-row group, i.e. row
   // i / 9, chunk i % 9 of the row's last 8 chunks (the pad slot 8 repeats
   // chunk 7).
-  const int tl_row = lane / 9;
-  const int tl_chunk = (lane % 9) == 8 ? 7 : lane % 9;
-  const uint32_t tl_off = (uint32_t)(kMainRowBytes + tl_chunk * 16);
+  // (Recomputed where used from an opaque copy of the lane index: a
+  // per-lane constant held across the tile loop would be spilled, and its
+  // reload would wait for every tile load in flight.)
+  auto tail_lane = [&](int& row, uint32_t& off) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    row = l / 9;
+    const int chunk = (l % 9) == 8 ? 7 : l % 9;
+    off = (uint32_t)(kMainRowBytes + chunk * 16);
+  };
 
   // Issue the direct-to-LDS loads of tile `tile` into buffer `buf`: this
   // wave's kRowsPerWave rows.  Rows past the shard end (last tile only) are
   // clamped to its last row.
-  auto issue = [&](int tile, int buf) {
+  auto issue = [&](int tile, int buf) __attribute__((always_inline)) {
     const int64_t base = s0 + (int64_t)tile * kTile;
     const uint32_t bufaddr = lds0 + (uint32_t)(buf * kBufBytes);
     const int64_t g0 = base + kRowsPerWave * wave;   // this wave's first row (8-aligned)
     if (g0 + kRowsPerWave - 1 <= last) {
       // all 8 rows inside the shard; an aligned 8-row group is 8 consecutive
       // physical rows in every layout
-      const uint8_t* src = kdata + hrow(g0) * kRowBytes;
+      const uint8_t* src = uniform_ptr(kdata + hrow(g0) * kRowBytes);
 #pragma unroll
       for (int k = 0; k < kRowsPerWave; ++k) {
         const int r = kRowsPerWave * wave + k;
@@ -197,6 +220,9 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
         const int r0 = kRowsPerWave * wave + 4 * h;
         const uint32_t m0 =
             __builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(kMainBytes + r0 * kTailStride * 16));
+        int tl_row;
+        uint32_t tl_off;
+        tail_lane(tl_row, tl_off);
         if (lane < 36) lds_dma16<true>(m0, src + 4 * h * kRowBytes, (uint32_t)(tl_row * kRowBytes) + tl_off);
       }
     } else {
@@ -207,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
         int64_t row = base + r;
         row = row < last ? row : last;
         lds_dma16<true>(__builtin_amdgcn_readfirstlane(bufaddr + (uint32_t)(r * kMainStride * 16)),
-                  kdata + hrow(row) * kRowBytes, (uint32_t)(lane * 16));
+                  uniform_ptr(kdata + hrow(row) * kRowBytes), (uint32_t)(lane * 16));
       }
 #pragma unroll
       for (int h = 0; h < kRowsPerWave / 4; ++h) {
@@ -218,10 +244,13 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
         // a 4-aligned group is 4 consecutive physical rows
         const int64_t row0 = base + r0;
         const int64_t rb = row0 < last ? row0 : last;
+        int tl_row;
+        uint32_t tl_off;
+        tail_lane(tl_row, tl_off);
         int64_t row = row0 + tl_row;
         row = row < last ? row : last;
         const uint32_t off = (uint32_t)((row - rb) * kRowBytes) + tl_off;
-        if (lane < 36) lds_dma16<true>(m0, kdata + hrow(rb) * kRowBytes, off);
+        if (lane < 36) lds_dma16<true>(m0, uniform_ptr(kdata + hrow(rb) * kRowBytes), off);
       }
     }
   };
@@ -275,16 +304,13 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   // a wave's columns hold a larger one, the shard is rerun with that wave's V
   // scaled by a power of two (vsc) that brings them into fp16's range, and
   // the wave's output scaled back.
-  // Wait for tile `tile` (at most the loads of the two tiles issued after it
-  // still in flight), meet the other waves (its loads have landed for all of
-  // them, and all are done with the previous tile: its buffer and the
-  // weights in LDS), issue the loads kAhead tiles on; returns the tile's
-  // valid rows (kTile or more except at the end).
-  auto tile_ready = [&](int tile) {
-    const int after = ntiles - 1 - tile;
-    if (after >= 2) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoads));
-    } else if (after == 1) {
+  // Wait for tile `tile` (the loads of the tile issued after it may still be
+  // in flight), meet the other waves (its loads have landed for all of them,
+  // and all are done with the tile two back: its buffer and the weights in
+  // LDS), issue the loads kAhead tiles on into that buffer; returns the
+  // tile's valid rows (kTile or more except at the end).
+  auto tile_ready = [&](int tile) __attribute__((always_inline)) {
+    if (tile + 1 < ntiles) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -296,8 +322,10 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
   // Logits S^T[token, head] of the tile in buffer tb for its 32 tokens and
   // this wave's 32 heads: 36 chunks of 16 dims, K operands read kKAhead
   // chunks ahead (an LDS read under load takes longer than the 32-cycle
-  // MFMA).  Element e: token 8 (e / 4) + 4 h2 + e % 4, head l32.
-  auto tile_logits = [&](const uint8_t* tb, f32x16_t& sl) {
+  // MFMA).  Element e: token 8 (e / 4) + 4 h2 + e % 4, head l32.  `between`
+  // runs after MFMA step i (vector-ALU work that proceeds under the MFMAs);
+  // the scheduling fences keep each step's work where it is written.
+  auto tile_logits = [&](const uint8_t* tb, f32x16_t& sl, auto&& between) __attribute__((always_inline)) {
     auto kread = [&](int c) {
       const uint8_t* p = c < 32 ? tb + k_main + 32 * c : tb + k_tail + 32 * (c - 32);
       return *reinterpret_cast<const uint4*>(p);
@@ -317,11 +345,14 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
         logit_mfma(sl2, k0, qop[c], i == 1);
       else
         logit_mfma(sl, k0, qop[c], i == 0);
+      between(i);
+      __builtin_amdgcn_sched_barrier(0);
     }
     logit_mfma_drain(sl, sl2);
 #pragma unroll
     for (int e = 0; e < 16; ++e) sl[e] += sl2[e];
   };
+  auto no_work = [](int) {};
   // The tile's max logit of head l32 (tokens below nvalid), log2 domain.
   auto tile_max2 = [&](const f32x16_t& sl, int nvalid) {
     float tmax = -INFINITY;
@@ -354,65 +385,72 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
       for (int tile = 0; tile < ntiles; ++tile) {
         const int nvalid = tile_ready(tile);
         f32x16_t sl;
-        tile_logits(smem + (tile % kBufs) * kBufBytes, sl);
+        tile_logits(smem + (tile % kBufs) * kBufBytes, sl, no_work);
         m2 = fmaxf(m2, tile_max2(sl, nvalid));
       }
       __syncthreads();           // every wave is past its last LDS read
       max_only = false;          // m2 now holds each head's exact max
       continue;
     }
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int buf = tile % kBufs;
-      const int nvalid = tile_ready(tile);
-      const uint8_t* tb = smem + buf * kBufBytes;
-      f32x16_t sl;
-      tile_logits(tb, sl);
 
-      // ---- softmax weights of head l32: this lane's 16 tokens
-      // 8 (e / 4) + 4 h2 + e % 4, the other 16 in lane l ^ 32
-      float x[16];
+    // ---- softmax weights of head l32 for a tile's logits sl (valid rows
+    // nvalid): this lane's 16 tokens 8 (e / 4) + 4 h2 + e % 4, the other 16
+    // in lane l ^ 32, in kSoftPieces pieces.  P = 2^(x c2 - m + kPOffset) (masked
+    // logits give exp2(-inf) = 0), packed to fp16 toward zero and stored to
+    // LDS; lsum takes the exact weights, lsum16 the fp16 ones the PV product
+    // uses.
+    float tmax = -INFINITY, pbase = 0.f, pe = 0.f;
+    auto soft_piece = [&](int k, const f32x16_t& sl, int nvalid) __attribute__((always_inline)) {
+      auto xv = [&](int e) {
+        return (nvalid >= kTile || 8 * (e >> 2) + 4 * h2 + (e & 3) < nvalid) ? sl[e] : -INFINITY;
+      };
+      if (k == 0) {
+        tmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = sl[e];
-      if (nvalid < kTile) {
+        for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, xv(e));
+      } else if (k == 1) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = 8 * (e >> 2) + 4 * h2 + (e & 3) < nvalid ? x[e] : -INFINITY;
-      }
-      const float tmax2 = tile_max2(sl, nvalid);
-      if (m2 == -INFINITY) m2 = tmax2;      // first tile: acc is still zero
-      overflow |= (tmax2 > m2 + kHeadroom);
-      // P = 2^(x c2 - m + kPOffset) (masked logits give exp2(-inf) = 0),
-      // packed to fp16 toward zero; lsum takes the exact weights, lsum16 the
-      // fp16 ones the PV product uses
-      uint32_t ph[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p0 = fast_exp2(fmaf(x[2 * i], c2, kPOffset - m2));
-        const float p1 = fast_exp2(fmaf(x[2 * i + 1], c2, kPOffset - m2));
-        lsum += p0 + p1;
-        const h16x2_t pp = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+        for (int e = 8; e < 16; ++e) tmax = fmaxf(tmax, xv(e));
+        const float tmax2 = half_max(tmax) * c2;
+        if (m2 == -INFINITY) m2 = tmax2;      // first tile: acc is still zero
+        overflow |= (tmax2 > m2 + kHeadroom);
+        pbase = kPOffset - m2;
+      } else if ((k & 1) == 0) {
+        // weight of element 2 i
+        const int i = (k - 2) >> 1;
+        pe = fast_exp2(fmaf(xv(2 * i), c2, pbase));
+        lsum += pe;
+        asm volatile("" : "+v"(lsum), "+v"(pe));   // taken here, not deferred
+      } else {
+        // weight of element 2 i + 1; the pair to fp16, its sum, to LDS
+        const int i = (k - 3) >> 1;
+        const float p1 = fast_exp2(fmaf(xv(2 * i + 1), c2, pbase));
+        lsum += p1;
+        const h16x2_t pp = __builtin_amdgcn_cvt_pkrtz(pe, p1);
         lsum16 = __builtin_amdgcn_fdot2(pp, h16x2_t{(__fp16)1.0f, (__fp16)1.0f}, lsum16, false);
-        ph[i] = __builtin_bit_cast(uint32_t, pp);
+        asm volatile("" : "+v"(lsum), "+v"(lsum16));
+        *(__attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+            p_lds + (uint32_t)(((2 * wave + (i >> 2)) * 64 + lane) * 16 + 4 * (i & 3))) =
+            __builtin_bit_cast(uint32_t, pp);
       }
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        *(lds_u32x4*)(uintptr_t)(p_lds + (uint32_t)(((2 * wave + st) * 64 + lane) * 16)) =
-            u32x4_t{ph[4 * st], ph[4 * st + 1], ph[4 * st + 2], ph[4 * st + 3]};
-      // every wave's weights are in LDS
-      __syncthreads();
+    };
 
-      // ---- O^T += V^T P^T: this wave's 4 blocks of 32 value columns against
-      // the weights of all 4 head blocks, two 16-token steps each; V^T
-      // operands converted to fp16 one step ahead of their MFMAs
+    // ---- O^T += V^T P^T for the tile in buffer buf: this wave's 4 blocks of
+    // 32 value columns against the weights of all 4 head blocks, two 16-token
+    // steps each; V^T operands converted to fp16 one step ahead of their MFMAs
+    auto tile_pv = [&](int buf) __attribute__((always_inline)) {
+      const uint8_t* tb = smem + buf * kBufBytes;
       if (vscaled) {
         // rerun with this wave's V scaled by vsc (a V element beyond fp16):
         // scale its 128 columns of the tile in LDS, which only this wave
         // reads from here on (every logits read of the tile is done), exactly
         // (a power of two; bf16 keeps fp32's exponent range)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int c = 64 * i + lane;          // 16-byte chunk: row c / 16, column chunk c % 16
-          lds_u32x4* q16 = (lds_u32x4*)(uintptr_t)(lds0 + (uint32_t)(buf * kBufBytes) +
-                                                   (uint32_t)((c / 16) * kMainStride * 16 + 256 * wave + (c % 16) * 16));
+        // 16-byte chunk 64 i + lane: row 4 i + lane / 16, column chunk lane % 16
+        lds_u32x4* const q0 = (lds_u32x4*)(uintptr_t)(lds0 + (uint32_t)(buf * kBufBytes) +
+                                                      (uint32_t)((lane >> 4) * kMainStride * 16 + 256 * wave + (lane & 15) * 16));
+#pragma unroll 1
+        for (int i = 0; i < 8; ++i) {      // one chunk at a time: a rare path, kept light on registers
+          lds_u32x4* q16 = q0 + i * 4 * kMainStride;
           u32x4_t w = *q16;
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -430,30 +468,74 @@ __global__ __launch_bounds__(kThreads) void mla_mfma_kernel(PartialArgs a) {
                                                       (lds_s16x4_t*)(p + 8 * kMainStride * 16)));
         return u32x4_t{w0.x, w0.y, w1.x, w1.y};
       };
+      // bf16 -> fp16 of one V^T operand dword (two values), tracking |V|
+      auto vconv = [&](uint32_t w) {
+        const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+        vmax = fmaxf(fmaxf(vmax, fabsf(lo)), fabsf(hi));
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+      };
       u32x4_t pw[4][2];
 #pragma unroll
       for (int H = 0; H < 4; ++H)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
           pw[H][st] = *(const lds_u32x4*)(uintptr_t)(p_lds + (uint32_t)(((2 * H + st) * 64 + lane) * 16));
-      u32x4_t vn = vraw(0, 0);
+      // step ds = (d, st): the raw V^T operand is read two steps ahead and
+      // converted one step ahead, between the four MFMAs of the step before
+      u32x4_t vr1 = vraw(0, 1), va;
+      {
+        const u32x4_t vr0 = vraw(0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) va[k] = vconv(vr0[k]);
+      }
 #pragma unroll
       for (int ds = 0; ds < 8; ++ds) {
         const int d = ds >> 1, st = ds & 1;
-        const u32x4_t vr = vn;
-        if (ds + 1 < 8) vn = vraw((ds + 1) >> 1, (ds + 1) & 1);
-        u32x4_t vh;
+        u32x4_t vr2 = vr1;
+        if (ds + 2 < 8) vr2 = vraw((ds + 2) >> 1, (ds + 2) & 1);
+        u32x4_t vn = va;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lo = __uint_as_float(vr[k] << 16), hi = __uint_as_float(vr[k] & 0xFFFF0000u);
-          vmax = fmaxf(fmaxf(vmax, fabsf(lo)), fabsf(hi));
-          vh[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        for (int H = 0; H < 4; ++H) {
+          acc[d][H] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, va),
+                                                             __builtin_bit_cast(f16x8_t, pw[H][st]), acc[d][H], 0, 0, 0);
+          if (ds + 1 < 8) vn[H] = vconv(vr1[H]);
         }
-        const f16x8_t va = __builtin_bit_cast(f16x8_t, vh);
+        va = vn;
+        vr1 = vr2;
 #pragma unroll
-        for (int H = 0; H < 4; ++H)
-          acc[d][H] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, __builtin_bit_cast(f16x8_t, pw[H][st]), acc[d][H], 0, 0, 0);
+        for (int H = 0; H < 4; ++H) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then a conversion's vector-ALU work
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+
+    // Software pipeline over the tiles: the logits of tile t run with the
+    // softmax of tile t - 1 in their shadow; then, once every wave's weights
+    // are in LDS, the PV product of tile t - 1.  Only the last tile can be
+    // partial, so every softmax inside the loop is over a full tile.
+    if (ntiles > 0) {
+      f32x16_t sp;                              // logits of the previous tile
+      tile_ready(0);
+      tile_logits(smem, sp, no_work);
+      for (int tile = 1; tile < ntiles; ++tile) {
+        tile_ready(tile);
+        f32x16_t sl;
+        tile_logits(smem + (tile % kBufs) * kBufBytes, sl, [&](int i) {
+          if ((i & 1) == 0) soft_piece(i >> 1, sp, kTile);
+        });
+        __syncthreads();                        // every wave's weights are in LDS
+        tile_pv((tile - 1) % kBufs);
+        sp = sl;
+      }
+      // the last tile: its softmax, then its PV product
+      __syncthreads();                          // every wave is past the previous weights
+      const int nlast = (int)(s1 - (s0 + (int64_t)(ntiles - 1) * kTile));
+#pragma unroll
+      for (int k = 0; k < kSoftPieces; ++k) soft_piece(k, sp, nlast);
+      __syncthreads();
+      tile_pv((ntiles - 1) % kBufs);
     }
     // a V element of this wave's columns beyond fp16 (on the unscaled pass)
     if (!vscaled && __any(vmax >= 65520.0f)) overflow |= 2;
