@@ -197,6 +197,20 @@ struct Layout<kMXFP4> {
   __device__ static constexpr int chunk_d(int c, int g) { return 32 * g + 8 * c; }
 };
 
+// V of the fp8 and MXFP4 caches reaches the registers coalesced, 16 bytes
+// per lane per load (a 16-row half-tile is one load per lane for MXFP4, two
+// for fp8, where the PV operand layout would need four single-token loads of
+// 4 or 8 bytes: the address unit's time goes by load instruction, not by
+// byte), and is regrouped through a per-wave LDS patch when its tile is
+// computed.  Row stride in the patch: 16 (MXFP4) / 32 (fp8) pad bytes put the
+// four token groups a read instruction gathers on disjoint banks.
+template <int KV>
+struct VPatch {
+  static constexpr int kRow = Layout<KV>::kRowBytes + (KV == kMXFP4 ? 16 : 32);
+  static constexpr int kHalf = 16 * kRow;            // one half-tile
+  static constexpr int kWaveBytes = 2 * kHalf;       // a tile
+};
+
 // Raw (undecoded) registers of one 32-token tile for one lane.
 template <int KV>
 struct Raw {
@@ -446,6 +460,15 @@ void gqa_mfma_kernel(PartialArgs a) {
     __shared__ MergeLds st;
     mrg = &st;
   }
+  // fp8 / MXFP4 with the register ring: V loaded coalesced, regrouped
+  // through this wave's LDS patch (VPatch)
+  constexpr bool VT = KV != kBF16 && !LDSRING;
+  uint32_t vt_lds = 0;
+  if constexpr (VT) {
+    __shared__ __attribute__((aligned(16))) uint8_t vt_st[kWaves * VPatch<KV>::kWaveBytes];
+    vt_lds = (uint32_t)(uintptr_t)(lds_u8*)vt_st +
+             (uint32_t)(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * VPatch<KV>::kWaveBytes);
+  }
 
   const int lane = threadIdx.x & 63;
   // wave index as a scalar, so everything derived from it stays wave-uniform
@@ -594,6 +617,25 @@ void gqa_mfma_kernel(PartialArgs a) {
           for (int w = 0; w < 4; ++w) rw.k[u][4 * i + w] = v[w];
         }
         const auto rv = tile_rsrc(vdata + hr * ROW, 16 * ROW);
+        if constexpr (VT) {
+          // coalesced: byte 16 lane (+ 1024) of the half-tile, i.e. row
+          // 16 lane / ROW, regrouped by v_regroup when the tile is computed
+          const u32x4_t v0 = buf_load16<NT>(rv, (uint32_t)(16 * lane));
+          if constexpr (Lay::kVBytes == 4) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) rw.v[4 * u + w][0] = v0[w];
+          } else {
+            const u32x4_t v1 = buf_load16<NT>(rv, (uint32_t)(16 * lane + 1024));
+            rw.v[4 * u][0] = v0[0];
+            rw.v[4 * u][1] = v0[1];
+            rw.v[4 * u + 1][0] = v0[2];
+            rw.v[4 * u + 1][1] = v0[3];
+            rw.v[4 * u + 2][0] = v1[0];
+            rw.v[4 * u + 2][1] = v1[1];
+            rw.v[4 * u + 3][0] = v1[2];
+            rw.v[4 * u + 3][1] = v1[3];
+          }
+        } else
 #pragma unroll
         for (int e = 4 * u; e < 4 * u + 4; ++e) {   // token 16u + 4g + e%4
           const uint32_t off = voff + (uint32_t)((e % 4) * ROW);
@@ -811,7 +853,44 @@ void gqa_mfma_kernel(PartialArgs a) {
   using PartTile = std::false_type;
   using Clamped = std::true_type;     // issue: rows clamped to the shard, lane by lane
   using Unclamped = std::false_type;
-  auto compute = [&](const Raw<KV>& rw, int tile, auto mask_tag) {
+  // The V registers of a full tile (loaded coalesced) through the wave's LDS
+  // patch into the PV operand layout: rw.v[e] = columns kVBytes r16 .. of
+  // token 16 (e / 4) + 4g + e % 4, as the partial-tile loads give them.
+  // Wave-local: the wave's LDS operations run in order, no barrier.
+  auto v_regroup = [&](const Raw<KV>& rw) {
+    using P = VPatch<KV>;
+    Raw<KV> rt = rw;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // lane's 16 bytes at row 16 lane / ROW, byte 16 lane % ROW (+ 8 rows)
+      const uint32_t wr = vt_lds + (uint32_t)(u * P::kHalf + (16 * lane / ROW) * P::kRow + (16 * lane) % ROW);
+      if constexpr (Lay::kVBytes == 4) {
+        *(lds_u32x4*)(uintptr_t)wr = u4(rw.v[4 * u][0], rw.v[4 * u + 1][0], rw.v[4 * u + 2][0], rw.v[4 * u + 3][0]);
+      } else {
+        *(lds_u32x4*)(uintptr_t)wr = u4(rw.v[4 * u][0], rw.v[4 * u][1], rw.v[4 * u + 1][0], rw.v[4 * u + 1][1]);
+        *(lds_u32x4*)(uintptr_t)(wr + 8 * P::kRow) =
+            u4(rw.v[4 * u + 2][0], rw.v[4 * u + 2][1], rw.v[4 * u + 3][0], rw.v[4 * u + 3][1]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t rd = vt_lds + (uint32_t)((e / 4) * P::kHalf + (4 * g + e % 4) * P::kRow + Lay::kVBytes * r16);
+      if constexpr (Lay::kVBytes == 4) {
+        rt.v[e][0] = *(const lds_u32*)(uintptr_t)rd;
+      } else {
+        const u32x2_t v = *(const lds_u32x2*)(uintptr_t)rd;
+        rt.v[e][0] = v[0];
+        rt.v[e][1] = v[1];
+      }
+    }
+    return rt;
+  };
+  auto compute = [&](const Raw<KV>& rw_in, int tile, auto mask_tag) {
+    // full tiles (Unmasked) of fp8 / MXFP4 come coalesced
+    const Raw<KV> rw = [&] {
+      if constexpr (VT && !decltype(mask_tag)::value) return v_regroup(rw_in);
+      else return rw_in;
+    }();
     const int64_t base = s0 + (int64_t)tile * kTile;
     int nv[TW];
 #pragma unroll

@@ -44,7 +44,11 @@ template <int KV, bool PAGED, bool SOLO>
 hipError_t launch_one_token(const PartialArgs& a, dim3 grid, hipStream_t stream) {
   auto fn = gqa_mfma_kernel<KV, PAGED, true, 1, false, SOLO>;
   const size_t lds = SOLO ? stash_bytes<KV>() : (size_t)Layout<KV>::kLdsReserve;
-  static_assert(stash_bytes<KV>() <= 160 * 1024, "stash fits the LDS");
+  constexpr size_t kPatch = KV == kBF16 ? 0 : (size_t)kWaves * VPatch<KV>::kWaveBytes;   // static V patches
+  static_assert(stash_bytes<KV>() + kPatch <= 160 * 1024, "stash and V patches fit the LDS");
+  static_assert(sizeof(MergeLds) + Layout<KV>::kLdsReserve + kPatch <= 160 * 1024, "merge, reserve and V patches fit");
+  static_assert(Layout<KV>::kWavesPerEu == 1 || 2 * (stash_bytes<KV>() + kPatch) <= 160 * 1024,
+                "two workgroups per CU");
   if (lds > 64 * 1024) {
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
