@@ -38,24 +38,24 @@ METRIC = "KV-read HBM GB/s (% of 8 TB/s peak) + µs per layer decode step, B=8 S
 # counters were taken on).  Changed kernel code no longer matches, and the
 # bench then reports traffic as null.  Summaries are under profiles/.
 TRAFFIC = {
-    ("helix_fp8", "contiguous", 32, 1, "bf13adca9bbd9ae0"): 17211269834,
-    ("helix_fp8", "contiguous", 128, 1, "bf13adca9bbd9ae0"): 17281780756,
-    ("helix_fp8", "contiguous", 32, 4, "72c39fc00755a1a4"): 17249117166,
-    ("helix_fp8", "contiguous", 32, 3, "72c39fc00755a1a4"): 17231770591,
-    ("helix_fp8", "contiguous", 128, 4, "72c39fc00755a1a4"): 17458637806,
-    ("helix_mxfp4", "contiguous", 32, 1, "bf13adca9bbd9ae0"): 9162223241,
-    ("helix_mxfp4", "contiguous", 128, 1, "bf13adca9bbd9ae0"): 9236260755,
-    ("gqa_bf16_varlen", "contiguous", 16, 1, "bf13adca9bbd9ae0"): 3496245251,
-    ("mla_bf16", "contiguous", 32, 1, "778a9c2893ba45b9"): 4901145396,
+    ("helix_fp8", "contiguous", 32, 1, "1d5f897ac7d074ca"): 17210454343,
+    ("helix_fp8", "contiguous", 128, 1, "1d5f897ac7d074ca"): 17279497781,
+    ("helix_fp8", "contiguous", 32, 4, "36a0b514422612bd"): 17248988135,
+    ("helix_fp8", "contiguous", 32, 3, "36a0b514422612bd"): 17231752584,
+    ("helix_fp8", "contiguous", 128, 4, "36a0b514422612bd"): 17452535621,
+    ("helix_mxfp4", "contiguous", 32, 1, "1d5f897ac7d074ca"): 9157645548,
+    ("helix_mxfp4", "contiguous", 128, 1, "1d5f897ac7d074ca"): 9228298482,
+    ("gqa_bf16_varlen", "contiguous", 16, 1, "1d5f897ac7d074ca"): 3495787310,
+    ("mla_bf16", "contiguous", 32, 1, "86eb417c08c25790"): 4905784948,
 }
 # Fraction of the partial kernel's SIMD cycles with the matrix cores busy,
 # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs), from a
 # rocprofv3 --pmc run; same keys as TRAFFIC.
 MFMA_BUSY = {
-    ("mla_bf16", "contiguous", 32, 1, "778a9c2893ba45b9"): 0.3919,
-    ("helix_mxfp4", "contiguous", 32, 1, "bf13adca9bbd9ae0"): 0.2201,
-    ("helix_fp8", "contiguous", 32, 1, "bf13adca9bbd9ae0"): 0.1284,
-    ("helix_fp8", "contiguous", 32, 4, "72c39fc00755a1a4"): 0.3598,
+    ("mla_bf16", "contiguous", 32, 1, "86eb417c08c25790"): 0.4151,
+    ("helix_mxfp4", "contiguous", 32, 1, "1d5f897ac7d074ca"): 0.2206,
+    ("helix_fp8", "contiguous", 32, 1, "1d5f897ac7d074ca"): 0.1314,
+    ("helix_fp8", "contiguous", 32, 4, "36a0b514422612bd"): 0.3408,
 }
 _GQA_SOURCES = ("partial_gqa_mfma.hip", "gqa_mfma_kernel.hpp", "partial_gqa_mfma_tokens.hip")
 KERNEL_SOURCES = {"bf16": _GQA_SOURCES, "fp8": _GQA_SOURCES, "mxfp4": _GQA_SOURCES,

@@ -460,9 +460,10 @@ void gqa_mfma_kernel(PartialArgs a) {
     __shared__ MergeLds st;
     mrg = &st;
   }
-  // fp8 / MXFP4 with the register ring: V loaded coalesced, regrouped
-  // through this wave's LDS patch (VPatch)
-  constexpr bool VT = KV != kBF16 && !LDSRING;
+  // fp8 / MXFP4, one token, register ring: V loaded coalesced, regrouped
+  // through this wave's LDS patch (VPatch).  (The two-token instances, whose
+  // longer tile computation covers the loads, measured slower with it.)
+  constexpr bool VT = KV != kBF16 && !LDSRING && TW == 1;
   uint32_t vt_lds = 0;
   if constexpr (VT) {
     __shared__ __attribute__((aligned(16))) uint8_t vt_st[kWaves * VPatch<KV>::kWaveBytes];
